@@ -1,0 +1,228 @@
+"""Benchmark of DFlash block attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3_global_d512]
+
+A step is one whole dflash_block_attn call (attention kernel + split-KV
+combine) over one batch of the named synthetic workload, inputs resident in
+HBM.  Between steps a 1 GiB buffer is rewritten (outside the timed events) so
+that the 256 MB Infinity Cache does not hold K/V from the previous step.
+
+Printed (one JSON line): query-tokens/s over the timed steps, the achieved
+K/V HBM bandwidth of the attention kernel against the 8 TB/s peak, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query-tokens/s + K/V HBM GB/s (% of peak) for block attention, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_mfma_c3_global_d512.json")
+KERNEL_SOURCES = ["attn_mfma.hip", "device_common.h", "decomp.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "non_causal_block_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def visible_kv_bytes(wl) -> int:
+    """Algorithmic K/V bytes: every key some query of the block can see, K and V
+    rows of every kv-head read once.  With a window only keys from the first
+    query's window start onward count; otherwise all L + n keys."""
+    import numpy as np
+
+    L = wl.ctx_lens.astype(np.int64)
+    n = wl.block_lens.astype(np.int64)
+    lo = np.maximum(0, L - wl.window + 1) if wl.window > 0 else np.zeros_like(L)
+    U = np.where(n > 0, L + n - lo, 0)
+    return int(U.sum()) * wl.Hkv * wl.D * 2 * 2
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle (unchanged) on a bounded sample of the workload's rows."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build()
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+    all_rows = wl.total_q * wl.Hq
+    # calibrate on a few rows, then size the sample for ~budget_s of work
+    probe = rng.choice(all_rows, size=min(all_rows, max(threads, 8)), replace=False)
+    t0 = time.perf_counter()
+    oracle.run_workload(wl, rows=probe, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    per_row = dt / len(probe)
+    n_rows = int(min(all_rows, max(len(probe), budget_s / per_row)))
+    rows = np.sort(rng.choice(all_rows, size=n_rows, replace=False))
+    t0 = time.perf_counter()
+    oracle.run_workload(wl, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = n_rows / wl.Hq  # one query token = Hq output rows
+    return {"value": tokens / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} of {all_rows} (token, q-head) output rows drawn uniformly from {wl.name}, "
+                      f"fp64, {dt:.1f} s on {threads} threads"}
+
+
+def traffic_for(kernel_hash: str, launches_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_sha") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3_global_d512")
+    ap.add_argument("--kernel", choices=["auto", "mfma", "ref"], default="auto")
+    ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards by request / kv-head with no communication; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import non_causal_block_amd as nb
+    import workloads
+
+    if not os.path.exists(nb._lib.LIB_PATH):
+        from non_causal_block_amd import build as hipbuild
+        hipbuild.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    kernel = {"auto": nb.DFLASH_KERNEL_AUTO, "mfma": nb.DFLASH_KERNEL_MFMA, "ref": nb.DFLASH_KERNEL_REFERENCE}[
+        args.kernel]
+
+    print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
+    wl = workloads.make(args.config, poison=False)
+
+    def t16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, kp, vp = t16(wl.q), t16(wl.k_pages), t16(wl.v_pages)
+    pt = torch.from_numpy(wl.page_table).to(dev)
+    ctx = torch.from_numpy(wl.ctx_lens).to(dev)
+    blk = torch.from_numpy(wl.block_lens).to(dev)
+    causal = torch.from_numpy(wl.causal).to(dev)
+    out = torch.empty((wl.total_q, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    desc = nb.make_desc(num_reqs=wl.B, total_q=wl.total_q, max_block_len=int(wl.block_lens.max()),
+                        total_kv_len=wl.total_kv, page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req,
+                        num_pages=wl.num_pages, kernel=kernel, num_workgroups=args.num_workgroups)
+    plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+    flush = None if args.no_flush else torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    n_ev = args.warmup + args.steps
+    call0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    call1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    att0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    att1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(i):
+        if flush is not None:
+            flush.fill_(float(i))
+        desc.event_attn_begin, desc.event_attn_end = att0[i].cuda_event, att1[i].cuda_event
+        call0[i].record(stream)
+        st = nb.dflash_block_attn(q, kp, vp, pt, ctx, blk, wl.Hq, wl.Hkv, wl.D, causal, wl.window, wl.scale, out,
+                                  stream.cuda_stream, desc)
+        call1[i].record(stream)
+        if st != nb.DFLASH_OK:
+            raise nb.DFlashError(st, nb.dflash_last_error_message())
+
+    print(f"[bench] plan: kernel={plan.kernel} workgroups={plan.num_workgroups} rows/unit={plan.rows_per_unit} "
+          f"combine={plan.combine_workgroups} workspace={plan.workspace_bytes}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.warmup, n_ev):
+        step(i)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+
+    call_ms = np.array([call0[i].elapsed_time(call1[i]) for i in range(args.warmup, n_ev)])
+    att_ms = np.array([att0[i].elapsed_time(att1[i]) for i in range(args.warmup, n_ev)])
+    tokens = wl.total_q
+    value = tokens * args.steps / (call_ms.sum() / 1e3)
+    kv_bytes = visible_kv_bytes(wl)
+    att_s = att_ms.mean() / 1e3
+    achieved = kv_bytes / att_s / 1e9
+    call_gbps = kv_bytes / (call_ms.mean() / 1e3) / 1e9
+    print(f"[bench] call mean {call_ms.mean()*1e3:.1f} us (p10 {np.percentile(call_ms,10)*1e3:.1f}, "
+          f"p90 {np.percentile(call_ms,90)*1e3:.1f}); attention kernel mean {att_ms.mean()*1e3:.1f} us; "
+          f"K/V {kv_bytes/1e6:.1f} MB -> {achieved:.0f} GB/s kernel, {call_gbps:.0f} GB/s call; "
+          f"wall {t_wall:.3f} s", file=sys.stderr, flush=True)
+
+    khash = kernel_source_hash()
+    traffic = traffic_for(khash, kv_bytes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl)
+
+    cfg = workloads.CONFIGS[args.config]
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": float(call_ms.mean()),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.config, "description": cfg.description, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
+            "head_dim": wl.D, "query_tokens": tokens, "total_kv_tokens": wl.total_kv, "window": wl.window,
+            "page_size": wl.page_size, "seed": wl.seed, "kernel": args.kernel,
+            "attn_workgroups": plan.num_workgroups, "kv_bytes": kv_bytes,
+        },
+        "kv_hbm_gbps": call_gbps,
+        "kv_hbm_frac_of_peak": call_gbps / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel": "attn_mfma_kernel" if plan.kernel == nb.DFLASH_KERNEL_MFMA else "attn_ref_kernel",
+            "kernel_sha": khash,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,154 @@
+/*
+ * dflash_block_attn.h -- C ABI of the MI355X (gfx950) DFlash block-attention library.
+ *
+ * The operation (kenforever1, "DFlash + Gemma 4 31B-it" notes, sections "what
+ * DFlash is" and "why non-causal attention is needed"):  a block-diffusion
+ * drafter proposes a block of 1 + num_speculative_tokens query tokens per
+ * request.  The block's queries (bonus token + mask tokens) attend to the
+ * request's context K/V -- computed from the target model's hidden states --
+ * together with the block's own K/V, as one whole block, with no left-to-right
+ * restriction.  That non-causal mode is the default; vLLM PR #43445 ("Allow
+ * causal DFlash", sections "implementation" and "key code") adds a per-request
+ * causal flag that the attention backend interprets, and sliding-window
+ * DFlash variants exist (same report, "motivation").  Gemma 4 31B's global
+ * layers use head_dim 512, so the backend must take head sizes up to 512
+ * (kenforever1 notes, "Gemma 4 31B-it structure" and the PR #52 change table).
+ *
+ * Per request r: L = ctx_lens[r] context keys, n = block_lens[r] block queries,
+ * T = L + n keys (the block's own K/V are keys L..L+n-1; the caller has written
+ * them to the paged cache before the call).  Query i sits at position p = L+i.
+ * For q-head h the kv-head is h / (n_heads / n_kv_heads) (contiguous groups).
+ * Query i sees keys j with
+ *     lo_i <= j <= hi_i,   hi_i = causal[r] ? p : T-1,
+ *     lo_i = window > 0 ? max(0, p - window + 1) : 0
+ * and its output is the softmax(scale * q.k)-weighted mean of those keys' V.
+ *
+ * All functions are thread-safe.  None of them allocates device memory,
+ * synchronises a stream or reads device memory from the host.
+ */
+#ifndef DFLASH_BLOCK_ATTN_H
+#define DFLASH_BLOCK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_ABI_VERSION 1
+
+/* Return codes. */
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_ERR_INVALID_ARGUMENT = 1,   /* a host-checkable argument is wrong; nothing was enqueued */
+    DFLASH_ERR_UNSUPPORTED = 2,        /* valid problem this library does not run (e.g. head_dim > 512) */
+    DFLASH_ERR_WORKSPACE_TOO_SMALL = 3,/* desc->workspace_bytes below dflash_block_attn_workspace_size */
+    DFLASH_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} dflash_status;
+
+/* Kernel selection (desc->kernel). */
+#define DFLASH_KERNEL_AUTO 0       /* the MFMA kernel where it applies, else the reference kernel */
+#define DFLASH_KERNEL_REFERENCE 1  /* plain VALU kernel: any head_dim <= 512, slow; for checking */
+#define DFLASH_KERNEL_MFMA 2       /* MFMA kernel: instantiated for head_dim 128/256/512, other
+                                      head_dims run on the next larger one with zero-filled lanes */
+
+/*
+ * Host-side facts about one call.  Everything here is host memory; nothing in it
+ * is read from the device.  Hints that bound device-side values only steer the
+ * plan (work split, grid); results do not depend on them, except total_q, which
+ * must be >= sum(block_lens) (rows past total_q are not combined).
+ */
+typedef struct {
+    int32_t num_reqs;          /* B >= 0: entries in ctx_lens / block_lens / causal / page_table rows */
+    int32_t total_q;           /* >= sum(block_lens): rows of q and out                                 */
+    int32_t max_block_len;     /* >= max(block_lens) (0 = unknown); picks the row tiling                 */
+    int64_t total_kv_len;      /* >= sum(ctx_lens + block_lens) (0 = unknown); sizes the work split      */
+    int32_t page_size;         /* tokens per KV page, a power of two in [1, 1024] (16 is the tuned one)  */
+    int32_t max_pages_per_req; /* row stride (entries) of page_table, >= 1                               */
+    int64_t num_pages;         /* rows of k_pages / v_pages, >= 1                                        */
+    int32_t kernel;            /* DFLASH_KERNEL_* (0 = auto)                                             */
+    int32_t num_workgroups;    /* 0 = planner decides; >= 1 forces the attention grid (tests)            */
+    int32_t num_cus;           /* 0 = query the current device; > 0 plans for that many compute units    */
+    void*   workspace;         /* device scratch owned by the caller, 256-byte aligned                    */
+    size_t  workspace_bytes;   /* its size; must be >= dflash_block_attn_workspace_size(...)             */
+    void*   event_attn_begin;  /* optional hipEvent_t recorded on `stream` right before the attention   */
+    void*   event_attn_end;    /*   kernel and right after it (not around the combine); NULL = none     */
+} dflash_batch_desc;
+
+/* What the planner decided for a call (dflash_block_attn_plan). */
+typedef struct {
+    int32_t kernel;            /* DFLASH_KERNEL_REFERENCE or DFLASH_KERNEL_MFMA                         */
+    int32_t num_workgroups;    /* attention workgroups; each takes an equal run of key tiles             */
+    int32_t tile_keys;         /* keys per tile                                                         */
+    int32_t rows_per_unit;     /* query rows (block query x q-head of one kv-head) handled together    */
+    int32_t head_dim_padded;   /* head_dim rounded up to the kernel's instantiation                      */
+    int32_t combine_workgroups;/* grid of the split-KV combine (0 = not launched)                        */
+    size_t  workspace_bytes;   /* scratch the call needs                                                */
+} dflash_plan_info;
+
+/*
+ * dflash_block_attn -- block attention for a batch of requests.
+ *
+ *   q           device bf16 [total_q][n_heads][head_dim]; requests' blocks packed in order
+ *   k_pages     device bf16 [num_pages][page_size][n_kv_heads][head_dim]
+ *   v_pages     device bf16, same layout as k_pages
+ *   page_table  device int32 [num_reqs][max_pages_per_req]; entry j of row r is the physical page
+ *               holding keys [j*page_size, (j+1)*page_size) of request r; entries at or past
+ *               ceil((L+n)/page_size) are never read
+ *   ctx_lens    device int32 [num_reqs], L >= 0
+ *   block_lens  device int32 [num_reqs], n >= 0 (n = 0: the request produces nothing)
+ *   n_heads     Hq >= 1;  n_kv_heads  Hkv >= 1 with Hq % Hkv == 0
+ *   head_dim    D, a multiple of 8 in [8, 512]
+ *   causal      device uint8 [num_reqs] (non-zero = causal) or NULL = every request non-causal
+ *   window      sliding window in keys (<= 0: none), applies to every request of the call
+ *   scale       logit scale (finite), usually 1/sqrt(head_dim)
+ *   out         device bf16 [total_q][n_heads][head_dim]; written, never read
+ *   stream      hipStream_t to enqueue on (NULL = null stream)
+ *   desc        host struct above
+ *
+ * Output rows are rounded to bf16 with round-to-nearest-even from fp32 accumulation.
+ * The call is asynchronous: it validates, enqueues one attention kernel and, when
+ * some request's keys were split over several workgroups, one combine kernel, and
+ * returns.  Buffers must stay valid until the stream has run the work.  Concurrent
+ * calls need distinct workspaces.  On a non-OK return from validation nothing is
+ * enqueued and `out` is untouched.  Device-side values outside the stated ranges
+ * (negative lengths, page ids >= num_pages, L+n beyond max_pages_per_req*page_size)
+ * are undefined behaviour.
+ */
+int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                      const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
+                      int32_t head_dim, const uint8_t* causal, int32_t window, float scale, void* out,
+                      void* stream, const dflash_batch_desc* desc);
+
+/* Scratch bytes dflash_block_attn needs for this desc and shape (desc->workspace is ignored). */
+int dflash_block_attn_workspace_size(const dflash_batch_desc* desc, int32_t n_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, size_t* bytes);
+
+/* The plan dflash_block_attn would use (host only; nothing is launched). */
+int dflash_block_attn_plan(const dflash_batch_desc* desc, int32_t n_heads, int32_t n_kv_heads,
+                           int32_t head_dim, dflash_plan_info* plan);
+
+/*
+ * 1 if the library runs this head configuration -- in both non-causal and causal
+ * mode and with any window -- else 0.  A backend must declare non-causal support
+ * rather than silently run a causal mask (kenforever1 notes, "why non-causal
+ * attention is needed"; vLLM PR #43445 report, "key code", the non-causal
+ * assertion).
+ */
+int dflash_block_attn_supports(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim);
+
+/* Static text for a dflash_status value. */
+const char* dflash_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* dflash_last_error_message(void);
+
+/* DFLASH_ABI_VERSION of the built library. */
+int dflash_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_BLOCK_ATTN_H */

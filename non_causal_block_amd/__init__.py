@@ -1,0 +1,136 @@
+"""DFlash block attention on MI355X (gfx950).
+
+Thin Python layer over the C ABI of ``libdflash_attn.so`` (declared in
+include/dflash_block_attn.h).  Functions carry the C names and only marshal
+arguments; ``block_attn`` adds the allocation of ``out`` and the workspace
+with torch (device memory and the current stream are the only things torch
+provides here).
+
+The operation: each request's block of 1 + num_speculative_tokens queries
+attends to the request's context K/V plus the block's own K/V, non-causally
+by default, with a per-request causal flag and an optional sliding window
+(kenforever1 "DFlash + Gemma 4 31B-it" notes, "why non-causal attention is
+needed"; vLLM PR #43445 report).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+from . import _lib
+from ._lib import (DFLASH_ERR_HIP, DFLASH_ERR_INVALID_ARGUMENT, DFLASH_ERR_UNSUPPORTED,  # noqa: F401
+                   DFLASH_ERR_WORKSPACE_TOO_SMALL, DFLASH_KERNEL_AUTO, DFLASH_KERNEL_MFMA, DFLASH_KERNEL_REFERENCE,
+                   DFLASH_OK, dflash_batch_desc, dflash_plan_info)
+
+
+class DFlashError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{dflash_status_string(status)} ({status}): {message}")
+        self.status = status
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check(status: int) -> None:
+    if status != DFLASH_OK:
+        raise DFlashError(status, dflash_last_error_message())
+
+
+# ---- the C names -----------------------------------------------------------
+def dflash_abi_version() -> int:
+    return _lib.load().dflash_abi_version()
+
+
+def dflash_status_string(status: int) -> str:
+    return _lib.load().dflash_status_string(status).decode()
+
+
+def dflash_last_error_message() -> str:
+    return _lib.load().dflash_last_error_message().decode()
+
+
+def dflash_block_attn_supports(n_heads: int, n_kv_heads: int, head_dim: int) -> bool:
+    return bool(_lib.load().dflash_block_attn_supports(n_heads, n_kv_heads, head_dim))
+
+
+def dflash_block_attn_workspace_size(desc: dflash_batch_desc, n_heads: int, n_kv_heads: int, head_dim: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.load().dflash_block_attn_workspace_size(ctypes.byref(desc), n_heads, n_kv_heads, head_dim,
+                                                        ctypes.byref(out)))
+    return int(out.value)
+
+
+def dflash_block_attn_plan(desc: dflash_batch_desc, n_heads: int, n_kv_heads: int, head_dim: int) -> dflash_plan_info:
+    info = dflash_plan_info()
+    _check(_lib.load().dflash_block_attn_plan(ctypes.byref(desc), n_heads, n_kv_heads, head_dim, ctypes.byref(info)))
+    return info
+
+
+def dflash_block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads: int, n_kv_heads: int,
+                      head_dim: int, causal, window: int, scale: float, out, stream: Optional[int],
+                      desc: dflash_batch_desc) -> int:
+    """Raw call: tensors (or raw device addresses) in, status code out."""
+    return _lib.load().dflash_block_attn(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(ctx_lens),
+                                         _ptr(block_lens), n_heads, n_kv_heads, head_dim, _ptr(causal), window,
+                                         scale, _ptr(out), stream, ctypes.byref(desc))
+
+
+# ---- convenience -------------------------------------------------------------
+def make_desc(*, num_reqs: int, total_q: int, max_block_len: int, total_kv_len: int, page_size: int,
+              max_pages_per_req: int, num_pages: int, kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0,
+              num_cus: int = 0) -> dflash_batch_desc:
+    d = dflash_batch_desc()
+    d.num_reqs = num_reqs
+    d.total_q = total_q
+    d.max_block_len = max_block_len
+    d.total_kv_len = total_kv_len
+    d.page_size = page_size
+    d.max_pages_per_req = max_pages_per_req
+    d.num_pages = num_pages
+    d.kernel = kernel
+    d.num_workgroups = num_workgroups
+    d.num_cus = num_cus
+    return d
+
+
+def block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, *, causal=None, window: int = 0,
+               scale: Optional[float] = None, out=None, max_block_len: int = 0, total_kv_len: int = 0,
+               kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0, workspace=None):
+    """Block attention on torch device tensors; returns ``out`` (bf16 [total_q, Hq, D]).
+
+    q: bf16 [total_q, Hq, D]; k_pages/v_pages: bf16 [num_pages, page_size, Hkv, D];
+    page_table: int32 [B, max_pages_per_req]; ctx_lens/block_lens: int32 [B];
+    causal: uint8 [B] or None.  ``max_block_len``/``total_kv_len`` are host hints
+    (0 = unknown).  Runs on torch's current stream.
+    """
+    import torch
+
+    total_q, Hq, D = q.shape
+    num_pages, page_size, Hkv, D2 = k_pages.shape
+    if D2 != D or v_pages.shape != k_pages.shape:
+        raise ValueError("q / k_pages / v_pages head_dim or shape mismatch")
+    B = ctx_lens.shape[0]
+    desc = make_desc(num_reqs=B, total_q=total_q, max_block_len=max_block_len, total_kv_len=total_kv_len,
+                     page_size=page_size, max_pages_per_req=page_table.shape[1], num_pages=num_pages,
+                     kernel=kernel, num_workgroups=num_workgroups)
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    need = dflash_block_attn_workspace_size(desc, Hq, Hkv, D)
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(dflash_block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, Hq, Hkv, D, causal, window,
+                             scale, out, stream, desc))
+    return out

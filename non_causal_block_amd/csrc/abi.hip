@@ -1,0 +1,333 @@
+// abi.hip -- the C ABI: host validation, planning and kernel launch.
+//
+// The operation and its arguments are described in include/dflash_block_attn.h.
+// Host-checkable mistakes are rejected before anything is enqueued and the
+// library never silently runs a different mask: a backend that cannot honour
+// the non-causal block must refuse it (kenforever1 "DFlash + Gemma 4 31B-it"
+// notes, "why non-causal attention is needed"; vLLM PR #43445 report, "key
+// code", the non-causal assertion and its message).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "dflash_block_attn.h"
+#include "decomp.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x)
+{
+    int s = 0;
+    while ((int64_t(1) << s) < x)
+        ++s;
+    return s;
+}
+
+// Compute-unit count per device, queried once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_cu_mu;
+int g_cu_count[kMaxDevices] = {0};
+
+int device_cus(int* out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return fail(DFLASH_ERR_HIP, "no current HIP device to plan for (set desc->num_cus to plan without one)");
+    if (dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lk(g_cu_mu);
+        if (g_cu_count[dev] > 0) {
+            *out = g_cu_count[dev];
+            return DFLASH_OK;
+        }
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return fail(DFLASH_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed on device %d", dev);
+    if (dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lk(g_cu_mu);
+        g_cu_count[dev] = cus;
+    }
+    *out = cus;
+    return DFLASH_OK;
+}
+
+constexpr int kMinTilesPerWg = 8;  // below this, fewer workgroups and fewer partials
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int kernel = 0;
+    int P = 0;
+    int tk = 0;
+    int rmax = 0;
+    int row_tiles = 0;
+    int Dp = 0;
+    int combine_wgs = 0;
+    size_t off_lse = 0;
+    size_t ws_bytes = 0;
+    bool empty = false;
+};
+
+int check_shape(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim)
+{
+    if (n_heads < 1 || n_kv_heads < 1)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "n_heads (%d) and n_kv_heads (%d) must be >= 1", n_heads, n_kv_heads);
+    if (n_heads % n_kv_heads != 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "n_heads (%d) must be a multiple of n_kv_heads (%d)", n_heads,
+                    n_kv_heads);
+    if (head_dim <= 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "head_dim (%d) must be positive", head_dim);
+    if (head_dim > 512)
+        return fail(DFLASH_ERR_UNSUPPORTED, "head_dim %d > 512 is not supported (head_size <= 512)", head_dim);
+    if (head_dim % 8 != 0)
+        return fail(DFLASH_ERR_UNSUPPORTED, "head_dim %d is not a multiple of 8", head_dim);
+    return DFLASH_OK;
+}
+
+int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D, Plan* p)
+{
+    if (!desc)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "desc is NULL");
+    int st = check_shape(Hq, Hkv, D);
+    if (st != DFLASH_OK)
+        return st;
+    if (desc->num_reqs < 0 || desc->total_q < 0 || desc->max_block_len < 0 || desc->total_kv_len < 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "negative count in desc (num_reqs %d, total_q %d, max_block_len %d)",
+                    desc->num_reqs, desc->total_q, desc->max_block_len);
+    if (!is_pow2(desc->page_size) || desc->page_size > 1024)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two in [1, 1024]", desc->page_size);
+    if (desc->max_pages_per_req < 1)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "max_pages_per_req %d must be >= 1", desc->max_pages_per_req);
+    if (desc->num_pages < 1)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_pages %lld must be >= 1", (long long)desc->num_pages);
+    if (desc->kernel < DFLASH_KERNEL_AUTO || desc->kernel > DFLASH_KERNEL_MFMA)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "unknown kernel selector %d", desc->kernel);
+    if (desc->num_workgroups < 0 || desc->num_cus < 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_workgroups / num_cus must be >= 0");
+
+    *p = Plan();
+    if (desc->num_reqs == 0 || desc->total_q == 0) {
+        p->empty = true;
+        return DFLASH_OK;
+    }
+    const int32_t G = Hq / Hkv;
+    const int kernel = desc->kernel == DFLASH_KERNEL_AUTO ? DFLASH_KERNEL_MFMA : desc->kernel;
+    int occ = 1;
+    if (kernel == DFLASH_KERNEL_MFMA) {
+        p->Dp = D <= 128 ? 128 : (D <= 256 ? 256 : 512);
+        p->tk = dflash::mfma_tile_keys();
+        const int rt_max = dflash::mfma_max_row_tiles(p->Dp);
+        int rt = rt_max;
+        if (desc->max_block_len > 0) {
+            const int64_t rows = (int64_t)desc->max_block_len * G;
+            rt = (int)std::min<int64_t>(rt_max, (rows + 15) / 16);
+        }
+        p->row_tiles = rt;
+        p->rmax = 16 * rt;
+    } else {
+        p->Dp = D;
+        p->tk = dflash::ref_tile_keys();
+        p->rmax = dflash::ref_rows_per_unit();
+        p->row_tiles = 0;
+    }
+    p->kernel = kernel;
+
+    int cus = desc->num_cus;
+    if (cus == 0) {
+        st = device_cus(&cus);
+        if (st != DFLASH_OK)
+            return st;
+        // resident workgroups per CU of the chosen kernel on this device
+        const int q = kernel == DFLASH_KERNEL_MFMA ? dflash::mfma_wgs_per_cu(p->Dp, p->row_tiles, D == p->Dp)
+                                                   : dflash::ref_wgs_per_cu();
+        if (q > 0)
+            occ = q;
+    }
+    int64_t P = (int64_t)cus * occ;
+    if (desc->total_kv_len > 0) {
+        const int64_t B = desc->num_reqs;
+        const int64_t keys = desc->total_kv_len;
+        int64_t groups = 1;
+        if (desc->max_block_len > 0)
+            groups = ((int64_t)desc->max_block_len * G + p->rmax - 1) / p->rmax;
+        const int64_t tiles = (int64_t)Hkv * groups * (keys / p->tk + B);
+        P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles + kMinTilesPerWg - 1) / kMinTilesPerWg));
+    }
+    if (desc->num_workgroups > 0)
+        P = desc->num_workgroups;
+    if (P > (1 << 20))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_workgroups %lld too large", (long long)P);
+    p->P = (int)P;
+    if (p->P > 1) {
+        const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(float);
+        p->off_lse = align_up(o_bytes);
+        p->ws_bytes = p->off_lse + align_up((size_t)p->P * 2 * p->rmax * sizeof(float));
+        p->combine_wgs = dflash::combine_grid((int64_t)desc->total_q * Hq);
+    }
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+const char* dflash_status_string(int status)
+{
+    switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported";
+    case DFLASH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DFLASH_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char* dflash_last_error_message(void) { return g_last_error; }
+
+int dflash_block_attn_supports(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim)
+{
+    char saved[sizeof g_last_error];
+    memcpy(saved, g_last_error, sizeof saved);
+    const int ok = check_shape(n_heads, n_kv_heads, head_dim) == DFLASH_OK;
+    memcpy(g_last_error, saved, sizeof saved);
+    return ok ? 1 : 0;
+}
+
+int dflash_block_attn_workspace_size(const dflash_batch_desc* desc, int32_t n_heads, int32_t n_kv_heads,
+                                     int32_t head_dim, size_t* bytes)
+{
+    if (!bytes)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "bytes is NULL");
+    Plan p;
+    const int st = make_plan(desc, n_heads, n_kv_heads, head_dim, &p);
+    if (st != DFLASH_OK)
+        return st;
+    *bytes = p.ws_bytes;
+    return DFLASH_OK;
+}
+
+int dflash_block_attn_plan(const dflash_batch_desc* desc, int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                           dflash_plan_info* info)
+{
+    if (!info)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "plan is NULL");
+    Plan p;
+    const int st = make_plan(desc, n_heads, n_kv_heads, head_dim, &p);
+    if (st != DFLASH_OK)
+        return st;
+    info->kernel = p.kernel;
+    info->num_workgroups = p.P;
+    info->tile_keys = p.tk;
+    info->rows_per_unit = p.rmax;
+    info->head_dim_padded = p.Dp;
+    info->combine_workgroups = p.combine_wgs;
+    info->workspace_bytes = p.ws_bytes;
+    return DFLASH_OK;
+}
+
+int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                      const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
+                      int32_t head_dim, const uint8_t* causal, int32_t window, float scale, void* out,
+                      void* stream, const dflash_batch_desc* desc)
+{
+    Plan p;
+    int st = make_plan(desc, n_heads, n_kv_heads, head_dim, &p);
+    if (st != DFLASH_OK)
+        return st;
+    if (!std::isfinite(scale))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (p.empty)
+        return DFLASH_OK;
+    if (!q || !k_pages || !v_pages || !page_table || !ctx_lens || !block_lens || !out)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "NULL device pointer (q %p, k_pages %p, v_pages %p, page_table %p, "
+                    "ctx_lens %p, block_lens %p, out %p)", q, k_pages, v_pages, page_table, ctx_lens, block_lens, out);
+    auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
+    if (mis16(q) || mis16(k_pages) || mis16(v_pages) || mis16(out))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(block_lens) & 3u))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "page_table, ctx_lens and block_lens must be 4-byte aligned");
+    if (p.ws_bytes > 0) {
+        if (!desc->workspace || desc->workspace_bytes < p.ws_bytes)
+            return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes at %p; this call needs %zu bytes",
+                        desc->workspace_bytes, desc->workspace, p.ws_bytes);
+        if (reinterpret_cast<uintptr_t>(desc->workspace) % kAlign)
+            return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    }
+
+    dflash::AttnArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_pages = static_cast<const uint16_t*>(k_pages);
+    a.v_pages = static_cast<const uint16_t*>(v_pages);
+    a.page_table = page_table;
+    a.ctx_lens = ctx_lens;
+    a.block_lens = block_lens;
+    a.causal = causal;
+    a.out = static_cast<uint16_t*>(out);
+    a.part_o = p.ws_bytes ? static_cast<float*>(desc->workspace) : nullptr;
+    a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(desc->workspace) + p.off_lse) : nullptr;
+    a.d.B = desc->num_reqs;
+    a.d.Hkv = n_kv_heads;
+    a.d.G = n_heads / n_kv_heads;
+    a.d.window = window;
+    a.d.rmax = p.rmax;
+    a.d.tk = p.tk;
+    a.d.P = p.P;
+    a.Hq = n_heads;
+    a.D = head_dim;
+    a.Dp = p.Dp;
+    a.page_shift = ilog2(desc->page_size);
+    a.max_pages_per_req = desc->max_pages_per_req;
+    a.scale_log2 = scale * 1.4426950408889634f;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (desc->event_attn_begin && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_begin), s) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_begin) failed");
+    hipError_t e = p.kernel == DFLASH_KERNEL_MFMA ? dflash::launch_attn_mfma(a, p.Dp, p.row_tiles, s)
+                                                  : dflash::launch_attn_ref(a, s);
+    if (e != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+    if (desc->event_attn_end && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_end), s) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_end) failed");
+    if (p.combine_wgs > 0) {
+        dflash::CombineArgs c;
+        c.ctx_lens = ctx_lens;
+        c.block_lens = block_lens;
+        c.part_o = a.part_o;
+        c.part_lse = a.part_lse;
+        c.out = a.out;
+        c.d = a.d;
+        c.Hq = n_heads;
+        c.D = head_dim;
+        c.Dp = p.Dp;
+        c.total_rows = (int64_t)desc->total_q * n_heads;
+        e = dflash::launch_combine(c, p.combine_wgs, s);
+        if (e != hipSuccess)
+            return fail(DFLASH_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return DFLASH_OK;
+}
+
+}  // extern "C"

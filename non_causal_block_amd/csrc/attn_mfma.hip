@@ -1,0 +1,613 @@
+// attn_mfma.hip -- the MFMA (matrix-core) block-attention kernel for gfx950.
+//
+// What it computes: kenforever1 "DFlash + Gemma 4 31B-it" notes, "why
+// non-causal attention is needed" -- each request's block of 1+k queries
+// attends, as a whole, to the context K/V plus the block's own K/V; the
+// causal variant lets query i see only itself and keys to its left; vLLM PR
+// #43445 (report, "implementation") makes causality a per-request flag and
+// adds sliding-window DFlash.  Global layers need head_dim 512 (notes,
+// "Gemma 4 31B-it structure").
+//
+// How (gfx950, wave64, 4 waves per workgroup, one wave per SIMD):
+//  * Work: decomp.h -- each workgroup takes an equal run of 32-key tiles over
+//    all (request, kv-head, row group) units; all G q-heads of a kv-head and
+//    all n block queries share every K/V byte (rows = n*G, tiled by 16).
+//  * The head dimension is split over the 4 waves (DW = Dp/4 each).  Wave w
+//    streams only its d-slice of every key: K straight from HBM into MFMA
+//    A-operand registers (8 consecutive d of one key per lane, 16-byte loads),
+//    V into registers and from there into a wave-private LDS tile.
+//  * S^T = K Q^T per wave over its d-slice with v_mfma_f32_16x16x32_bf16
+//    (A = K, rows = keys; B = Q^T, held for the whole unit); the four partial
+//    S^T tiles are summed through LDS by the wave that owns the row tile, which
+//    applies the mask, runs the softmax (exp2; max over lanes with
+//    xor-shuffles) and publishes P^T in exactly the MFMA B-operand layout.
+//  * O^T += V^T P^T per wave for its d-slice (A = V^T gathered from LDS, B =
+//    P^T from LDS), fp32 accumulators in registers.
+//  * No rescaling of the accumulators: a row's reference max is its first
+//    visible tile's max, kept while later tiles stay within 2^32 of it (the
+//    probabilities then fit bf16/fp32 comfortably).  A tile beyond that
+//    (extreme logit ranges only) abandons the segment; after its run the
+//    workgroup recomputes such segments with each row's exact max found by a
+//    K-only pass.  Numerator and denominator share the reference, so the
+//    result is the same softmax either way.
+//  * K/V rows of keys past the request's end are zeroed (V) or masked (K), so
+//    page-tail garbage cannot reach the output through 0*NaN.
+//  * Epilogue: a unit finished inside the workgroup writes bf16 output;
+//    otherwise fp32 normalised partials + log2-sum-exp for combine.hip.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dflash {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTK = 32;              // keys per tile (two 16-key MFMA tiles)
+constexpr float kLazyBound = 32.0f;  // log2 units a row max may exceed its reference by
+constexpr int kLazy = 0, kMaxScan = 1, kFixed = 2;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p)
+{
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even)
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int DP, int RT>
+struct Cfg {
+    static constexpr int DW = DP / kWaves;  // d per wave
+    static constexpr int KS = DW / 32;      // QK^T k-steps per wave
+    static constexpr int DT = DW / 16;      // PV d-tiles per wave
+    static constexpr int ROWS = 16 * RT;
+    static constexpr int NOWN = (RT + kWaves - 1) / kWaves;  // row tiles owned per wave
+    // With head_dim 512 and 4-5 row tiles the Q^T operands live in LDS, not registers:
+    // the register file cannot hold them next to the 128-160 accumulators.
+    static constexpr bool QLDS = DP == 512 && RT >= 4;
+    // V tile, row-major [key][d_local]; transposed reads walk down a column and the
+    // 8-byte row pad spreads the four lane groups over different banks
+    static constexpr int VROW = DW * 2 + 8;
+    // LDS layout (bytes)
+    static constexpr int SX_BYTES = kWaves * 2 * RT * 64 * 16;  // partial S^T [wave][h][b][lane]
+    static constexpr int PX_BYTES = RT * 64 * 16;               // P^T (B operand) [b][lane]
+    static constexpr int V_BYTES_PER_WAVE = kTK * VROW;
+    static constexpr int V_BYTES = kWaves * V_BYTES_PER_WAVE;
+    static constexpr int ROWF_BYTES = ROWS * 4;
+    static constexpr int OFF_SX = 0;
+    static constexpr int OFF_PX = OFF_SX + SX_BYTES;
+    static constexpr int OFF_V = OFF_PX + PX_BYTES;
+    static constexpr int OFF_LSUM = OFF_V + V_BYTES;
+    static constexpr int OFF_MREF = OFF_LSUM + ROWF_BYTES;
+    static constexpr int OFF_FLAG = OFF_MREF + ROWF_BYTES;
+    static constexpr int OFF_Q = OFF_FLAG + 16 * 4;
+    static constexpr int Q_BYTES = QLDS ? RT * KS * kThreads * 16 : 0;
+    static constexpr int LDS_BYTES = OFF_Q + Q_BYTES;
+    static_assert(KS >= 1 && DT >= 1, "head_dim too small for the d-split");
+    static_assert(RT <= 16, "flag array");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// EXACT: head_dim == DP, so every d-chunk exists and no lane needs masking.
+template <int DP, int RT, bool EXACT>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
+{
+    using C = Cfg<DP, RT>;
+    constexpr int KS = C::KS;
+    constexpr int DT = C::DT;
+    constexpr int DW = C::DW;
+    constexpr int NOWN = C::NOWN;
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    f32x4_t* sx = reinterpret_cast<f32x4_t*>(lds + C::OFF_SX);
+    u32x4_t* px = reinterpret_cast<u32x4_t*>(lds + C::OFF_PX);
+    float* lsum_s = reinterpret_cast<float*>(lds + C::OFF_LSUM);
+    float* mref_s = reinterpret_cast<float*>(lds + C::OFF_MREF);
+    int* flag_s = reinterpret_cast<int*>(lds + C::OFF_FLAG);
+    u32x4_t* qls = reinterpret_cast<u32x4_t*>(lds + C::OFF_Q);  // [b][s][thread] when QLDS
+
+    const Decomp& d = a.d;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15;
+    const int grp4 = lane >> 4;
+    const int wbase = wave * DW;  // first d of this wave's slice
+    unsigned char* vls = lds + C::OFF_V + wave * C::V_BYTES_PER_WAVE;
+
+    const int32_t wg = logical_wg(blockIdx.x, d.P);
+    const int32_t D = a.D;
+    const int32_t G = d.G;
+    const int32_t psize = 1 << a.page_shift;
+
+    // d-chunks of this lane that exist (all of them unless head_dim < padded head_dim)
+    bool dval[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+        dval[s] = EXACT || (wbase + 32 * s + 8 * grp4 < D);
+
+    const int64_t total = wave_total_work(a.ctx_lens, a.block_lens, d);
+    const int64_t tpw = tiles_per_wg(total, d.P);
+    const int64_t begin = (int64_t)wg * tpw;
+    const int64_t end = min(total, begin + tpw);
+    if (begin >= end)
+        return;
+
+    int32_t r_first;
+    int64_t rbase_first;
+    wave_find_request(a.ctx_lens, a.block_lens, d, begin, r_first, rbase_first);
+    int64_t qstart_first = 0;  // first query token of request r_first
+    for (int32_t base = 0; base < r_first; base += 64) {
+        int64_t nn = (base + lane < r_first) ? (int64_t)a.block_lens[base + lane] : 0;
+        qstart_first += shfl_i64(wave_inclusive_scan(nn), 63);
+    }
+
+    // Segments of this workgroup's run that a lazy pass abandoned (bit i: i-th segment;
+    // segments past 63 share the overflow flag and are all recomputed).
+    uint64_t redo_mask = 0;
+    bool redo_overflow = false;
+
+    f32x4_t o[DT][RT];
+    float m_run[NOWN];
+    float l_run[NOWN];
+
+    // Walks the run; phase 0 runs every segment lazily, phase 1 recomputes abandoned ones.
+    auto walk = [&](auto phase_tag) {
+        constexpr int PHASE = decltype(phase_tag)::value;
+        int32_t r = r_first;
+        int64_t rbase = rbase_first;
+        int64_t qstart = qstart_first;
+        int64_t pos = begin;
+        int seg = 0;
+        while (pos < end) {
+            const int32_t L = a.ctx_lens[r];
+            const int32_t n = a.block_lens[r];
+            const ReqGeom g = req_geom(L, n, d);
+            const int64_t w = req_work(g, d);
+            if (pos >= rbase + w) {
+                rbase += w;
+                qstart += n;
+                ++r;
+                continue;
+            }
+            const int64_t off = pos - rbase;
+            const int32_t unit = (int32_t)(off / g.ntiles);
+            const int32_t t0 = (int32_t)(off % g.ntiles);
+            const int64_t seg_end = min(end, rbase + (int64_t)(unit + 1) * g.ntiles);
+            const int32_t t1 = (int32_t)(seg_end - rbase - (int64_t)unit * g.ntiles);
+            const int this_seg = seg++;
+            pos = seg_end;
+            if constexpr (PHASE == 1) {
+                const bool redo = this_seg < 64 ? ((redo_mask >> this_seg) & 1u) != 0 : redo_overflow;
+                if (!redo)
+                    continue;
+            }
+            const int32_t kvh = unit / g.ngroups;
+            const int32_t grp = unit % g.ngroups;
+            const int slot = (this_seg == 0) ? 0 : 1;
+            const bool whole = (t0 == 0 && t1 == g.ntiles);
+            const bool is_causal = a.causal ? (a.causal[r] != 0) : false;
+            const int32_t row0 = grp * d.rmax;
+            const int32_t rows_here = min(d.rmax, n * G - row0);
+            const int32_t T = g.T;
+            const int32_t* pt = a.page_table + (int64_t)r * a.max_pages_per_req;
+            // element offset of kv-head kvh inside a key row; d-chunks past head_dim
+            // address the row start instead (never past the row), and are zeroed
+            const int64_t head_off = (int64_t)kvh * D;
+
+            // ---------------- Q^T (B operand) for the unit ----------------
+            bf16x8_t qf[C::QLDS ? 1 : RT][KS];
+            if constexpr (C::QLDS)
+                __syncthreads();  // the previous segment may still read Q from LDS
+#pragma unroll
+            for (int b = 0; b < RT; ++b) {
+                const int32_t row = b * 16 + l16;
+                const bool rv = row < rows_here;
+                const int32_t rr = row0 + (rv ? row : 0);
+                const int32_t qi = rr / G;
+                const int32_t qj = rr % G;
+                const uint16_t* qrow = a.q + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    u32x4_t x = ldg16(qrow + (dval[s] ? wbase + 32 * s + 8 * grp4 : 0));
+                    const bool keep = rv && dval[s];
+                    x[0] = keep ? x[0] : 0u;
+                    x[1] = keep ? x[1] : 0u;
+                    x[2] = keep ? x[2] : 0u;
+                    x[3] = keep ? x[3] : 0u;
+                    if constexpr (C::QLDS)
+                        qls[(b * KS + s) * kThreads + threadIdx.x] = x;
+                    else
+                        qf[b][s] = as_bf16x8(x);
+                }
+            }
+
+            // Row offset (elements) of this lane's key in half h of tile t, and whether it
+            // exists.  Keys past the end use the request's first key row so that every load
+            // stays in bounds; their V is zeroed and their logits are masked.
+            const int64_t safe_row =
+                ((int64_t)pt[g.kv_lo >> a.page_shift] * psize + (g.kv_lo & (psize - 1))) * d.Hkv * (int64_t)D;
+            auto key_row = [&](int32_t t, int h, bool& valid) -> int64_t {
+                const int32_t key = g.kv_lo + t * kTK + 16 * h + l16;
+                valid = key < T;
+                if (!valid)
+                    return safe_row;
+                const int64_t page = pt[key >> a.page_shift];
+                return (page * psize + (key & (psize - 1))) * d.Hkv * (int64_t)D;
+            };
+
+            float m_fix[NOWN];
+#pragma unroll
+            for (int ob = 0; ob < NOWN; ++ob)
+                m_fix[ob] = -INFINITY;
+
+            // One pass over the segment's tiles (MODE kLazy, kMaxScan or kFixed).  Returns
+            // true when a kLazy pass met a tile beyond its reference bound.
+            auto run_pass = [&](auto mode_tag) -> bool {
+                constexpr int MODE = decltype(mode_tag)::value;
+                if constexpr (MODE != kMaxScan) {
+#pragma unroll
+                    for (int c = 0; c < DT; ++c)
+#pragma unroll
+                        for (int b = 0; b < RT; ++b)
+                            o[c][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int ob = 0; ob < NOWN; ++ob) {
+                    m_run[ob] = MODE == kFixed ? m_fix[ob] : -INFINITY;
+                    l_run[ob] = 0.f;
+                }
+                bool aborted = false;
+
+                int64_t krow[2], krow_next[2];
+                bool kval[2], kval_next[2];
+                u32x4_t kr[2][KS], vr[2][KS];
+                auto issue_kv = [&]() {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint16_t* kp = a.k_pages + krow[h] + head_off;
+                        const uint16_t* vp = a.v_pages + krow[h] + head_off;
+#pragma unroll
+                        for (int s = 0; s < KS; ++s) {
+                            const int e = (EXACT || dval[s]) ? wbase + 32 * s + 8 * grp4 : 0;
+                            kr[h][s] = ldg16(kp + e);
+                            if constexpr (MODE != kMaxScan)
+                                vr[h][s] = ldg16(vp + e);
+                        }
+                    }
+                };
+
+                // One 32-key tile per step: the registers of tile t are consumed first (V
+                // into LDS, K into the S^T MFMAs); then tile t+1 is requested into the same
+                // registers, so its loads overlap the softmax and PV product of tile t.
+                krow[0] = key_row(t0, 0, kval[0]);
+                krow[1] = key_row(t0, 1, kval[1]);
+                issue_kv();
+                if (t0 + 1 < t1) {
+                    krow_next[0] = key_row(t0 + 1, 0, kval_next[0]);
+                    krow_next[1] = key_row(t0 + 1, 1, kval_next[1]);
+                }
+                for (int32_t t = t0; t < t1; ++t) {
+                    const int32_t k0 = g.kv_lo + t * kTK;
+                    // (1) this wave's V slice -> LDS [key][d_local]; absent keys/d are zero
+                    if constexpr (MODE != kMaxScan) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int s = 0; s < KS; ++s) {
+                                const bool keep = kval[h] && dval[s];
+                                const u32x2_t lo2 = {keep ? vr[h][s][0] : 0u, keep ? vr[h][s][1] : 0u};
+                                const u32x2_t hi2 = {keep ? vr[h][s][2] : 0u, keep ? vr[h][s][3] : 0u};
+                                unsigned char* dst = vls + (16 * h + l16) * C::VROW + (32 * s + 8 * grp4) * 2;
+                                *reinterpret_cast<u32x2_t*>(dst) = lo2;
+                                *reinterpret_cast<u32x2_t*>(dst + 8) = hi2;
+                            }
+                    }
+                    // (2) partial S^T over this wave's d-slice (absent d: Q is zero there;
+                    //     absent keys are masked below, whatever their K holds)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int b = 0; b < RT; ++b) {
+                            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s = 0; s < KS; ++s) {
+                                u32x4_t kx = kr[h][s];
+                                kx[0] = dval[s] ? kx[0] : 0u;
+                                kx[1] = dval[s] ? kx[1] : 0u;
+                                kx[2] = dval[s] ? kx[2] : 0u;
+                                kx[3] = dval[s] ? kx[3] : 0u;
+                                if constexpr (C::QLDS)
+                                    acc = mfma16(as_bf16x8(kx), as_bf16x8(qls[(b * KS + s) * kThreads + threadIdx.x]),
+                                                 acc);
+                                else
+                                    acc = mfma16(as_bf16x8(kx), qf[b][s], acc);
+                            }
+                            sx[((wave * 2 + h) * RT + b) * 64 + lane] = acc;
+                        }
+                    // request tile t+1 (registers are free now), then the page entries of t+2
+                    if (t + 1 < t1) {
+                        krow[0] = krow_next[0];
+                        krow[1] = krow_next[1];
+                        kval[0] = kval_next[0];
+                        kval[1] = kval_next[1];
+                        issue_kv();
+                        if (t + 2 < t1) {
+                            krow_next[0] = key_row(t + 2, 0, kval_next[0]);
+                            krow_next[1] = key_row(t + 2, 1, kval_next[1]);
+                        }
+                    }
+                    __syncthreads();
+                    // (3) owners: reduce, mask, softmax, publish P^T
+#pragma unroll
+                    for (int ob = 0; ob < NOWN; ++ob) {
+                        const int b = ob * kWaves + wave;
+                        if (b < RT) {
+                            float z[8];
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                f32x4_t s4 = sx[((0 * 2 + h) * RT + b) * 64 + lane];
+#pragma unroll
+                                for (int ww = 1; ww < kWaves; ++ww)
+                                    s4 += sx[((ww * 2 + h) * RT + b) * 64 + lane];
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    z[h * 4 + e] = s4[e];
+                            }
+                            const int32_t row = b * 16 + l16;
+                            const bool rv = row < rows_here;
+                            const int32_t qi = (row0 + (rv ? row : 0)) / G;
+                            int32_t lo, hi;
+                            query_range(L, n, qi, is_causal, d.window, lo, hi);
+                            if (!rv)
+                                hi = -1;  // padding row: nothing visible
+                            float tmax = -INFINITY;
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const int32_t key = k0 + 16 * h + 4 * grp4 + e;
+                                    const bool vis = key >= lo && key <= hi;
+                                    const float zz = vis ? z[h * 4 + e] * a.scale_log2 : -INFINITY;
+                                    z[h * 4 + e] = zz;
+                                    tmax = fmaxf(tmax, zz);
+                                }
+                            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+                            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                            if constexpr (MODE == kMaxScan) {
+                                m_fix[ob] = fmaxf(m_fix[ob], tmax);
+                            } else {
+                                const float m_old = m_run[ob];
+                                float m_new = m_old;
+                                bool over = false;
+                                if constexpr (MODE == kLazy) {
+                                    const bool first = m_old == -INFINITY;
+                                    over = !first && tmax > m_old + kLazyBound;
+                                    m_new = first ? tmax : m_old;
+                                }
+                                const float mu = (m_new == -INFINITY) ? 0.f : m_new;
+                                u32x4_t pk;
+                                float psum = 0.f;
+#pragma unroll
+                                for (int e2 = 0; e2 < 4; ++e2) {
+                                    const uint32_t w2 =
+                                        pack_bf16x2(exp2f(z[2 * e2] - mu), exp2f(z[2 * e2 + 1] - mu));
+                                    pk[e2] = w2;
+                                    // the denominator sums the same bf16-rounded weights PV uses
+                                    psum += __uint_as_float(w2 << 16) + __uint_as_float(w2 & 0xffff0000u);
+                                }
+                                l_run[ob] += psum;
+                                m_run[ob] = m_new;
+                                px[b * 64 + lane] = pk;
+                                if constexpr (MODE == kLazy) {
+                                    const unsigned long long anyover = __ballot(over);
+                                    if (lane == 0)
+                                        flag_s[b] = anyover ? 1 : 0;
+                                }
+                            }
+                        }
+                    }
+                    __syncthreads();
+                    if constexpr (MODE == kMaxScan)
+                        continue;
+                    if constexpr (MODE == kLazy) {
+                        int anyover = 0;
+#pragma unroll
+                        for (int b = 0; b < RT; ++b)
+                            anyover |= flag_s[b];
+                        if (anyover) {
+                            aborted = true;
+                            break;
+                        }
+                    }
+                    // (4) O^T += V^T P^T for this wave's d-slice
+                    bf16x8_t pb[RT];
+#pragma unroll
+                    for (int b = 0; b < RT; ++b)
+                        pb[b] = as_bf16x8(px[b * 64 + lane]);
+#pragma unroll
+                    for (int c = 0; c < DT; ++c) {
+                        // A operand: V^T rows d = 16c + l16; key slots 4*grp4 + 0..3, 16 + 4*grp4 + 0..3
+                        const unsigned char* col = vls + (16 * c + l16) * 2;
+                        u32x4_t va;
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            const int k0e = (e2 < 2) ? (4 * grp4 + 2 * e2) : (16 + 4 * grp4 + 2 * (e2 - 2));
+                            const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(col + k0e * C::VROW);
+                            const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(col + (k0e + 1) * C::VROW);
+                            va[e2] = lo16 | (hi16 << 16);
+                        }
+                        const bf16x8_t vb = as_bf16x8(va);
+#pragma unroll
+                        for (int b = 0; b < RT; ++b)
+                            o[c][b] = mfma16(vb, pb[b], o[c][b]);
+                    }
+                }
+                // wait for the last tile's LDS traffic of every wave before anything reuses it
+                __syncthreads();
+                return aborted;
+            };
+
+            if constexpr (PHASE == 0) {
+                if (run_pass(std::integral_constant<int, kLazy>{})) {
+                    if (this_seg < 64)
+                        redo_mask |= (uint64_t)1 << this_seg;
+                    else
+                        redo_overflow = true;
+                    continue;  // recomputed after the run
+                }
+            } else {
+                run_pass(std::integral_constant<int, kMaxScan>{});
+                run_pass(std::integral_constant<int, kFixed>{});
+            }
+
+            // ---------------- epilogue ----------------
+#pragma unroll
+            for (int ob = 0; ob < NOWN; ++ob) {
+                const int b = ob * kWaves + wave;
+                if (b < RT) {
+                    float l = l_run[ob];
+                    l += __shfl_xor(l, 16);
+                    l += __shfl_xor(l, 32);
+                    if (grp4 == 0) {
+                        lsum_s[b * 16 + l16] = l;
+                        mref_s[b * 16 + l16] = m_run[ob];
+                    }
+                }
+            }
+            __syncthreads();
+            const int64_t sbase = ((int64_t)wg * 2 + slot) * d.rmax;
+#pragma unroll
+            for (int b = 0; b < RT; ++b) {
+                const int32_t row = b * 16 + l16;
+                if (row < rows_here) {
+                    const float l = lsum_s[row];
+                    const float inv = l > 0.f ? 1.f / l : 0.f;
+                    const int32_t rr = row0 + row;
+                    const int32_t qi = rr / G;
+                    const int32_t qj = rr % G;
+                    uint16_t* orow = a.out + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
+                    float* prow = a.part_o + (sbase + row) * a.Dp;
+#pragma unroll
+                    for (int c = 0; c < DT; ++c) {
+                        const int32_t dd = wbase + 16 * c + 4 * grp4;
+                        if (dd < D) {
+                            const f32x4_t v = o[c][b] * inv;
+                            if (whole) {
+                                const u32x2_t pk2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                                *reinterpret_cast<u32x2_t*>(orow + dd) = pk2;
+                            } else {
+                                *reinterpret_cast<f32x4_t*>(prow + dd) = v;
+                            }
+                        }
+                    }
+                    if (!whole && wave == 0 && grp4 == 0)
+                        a.part_lse[sbase + row] = l > 0.f ? mref_s[row] + log2f(l) : -INFINITY;
+                }
+            }
+            __syncthreads();
+        }
+    };
+
+    walk(std::integral_constant<int, 0>{});
+    if (redo_mask != 0 || redo_overflow)
+        walk(std::integral_constant<int, 1>{});
+}
+
+template <int DP, int RT, bool EXACT>
+static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
+{
+    using C = Cfg<DP, RT>;
+    auto kern = attn_mfma_kernel<DP, RT, EXACT>;
+    if (C::LDS_BYTES > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.d.P), dim3(kThreads), C::LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
+template <int DP, bool EXACT>
+static hipError_t launch_rt(const AttnArgs& a, int row_tiles, hipStream_t stream)
+{
+    switch (row_tiles) {
+    case 1: return launch_one<DP, 1, EXACT>(a, stream);
+    case 2: return launch_one<DP, 2, EXACT>(a, stream);
+    case 3: return launch_one<DP, 3, EXACT>(a, stream);
+    case 4: return launch_one<DP, 4, EXACT>(a, stream);
+    case 5: return launch_one<DP, 5, EXACT>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DP>
+static hipError_t launch_dp(const AttnArgs& a, int row_tiles, hipStream_t stream)
+{
+    return a.D == DP ? launch_rt<DP, true>(a, row_tiles, stream) : launch_rt<DP, false>(a, row_tiles, stream);
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream)
+{
+    switch (dpad) {
+    case 128: return launch_dp<128>(a, row_tiles, stream);
+    case 256: return launch_dp<256>(a, row_tiles, stream);
+    case 512: return launch_dp<512>(a, row_tiles, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DP, int RT, bool EXACT>
+static int occupancy_one()
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT>, kThreads,
+                                                     Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
+        return 0;
+    return blocks;
+}
+
+template <int DP, bool EXACT>
+static int occupancy_rt(int row_tiles)
+{
+    switch (row_tiles) {
+    case 1: return occupancy_one<DP, 1, EXACT>();
+    case 2: return occupancy_one<DP, 2, EXACT>();
+    case 3: return occupancy_one<DP, 3, EXACT>();
+    case 4: return occupancy_one<DP, 4, EXACT>();
+    case 5: return occupancy_one<DP, 5, EXACT>();
+    default: return 0;
+    }
+}
+
+int mfma_tile_keys() { return kTK; }
+int mfma_max_row_tiles(int /*dpad*/) { return 5; }
+
+int mfma_wgs_per_cu(int dpad, int row_tiles, bool exact)
+{
+    switch (dpad) {
+    case 128: return exact ? occupancy_rt<128, true>(row_tiles) : occupancy_rt<128, false>(row_tiles);
+    case 256: return exact ? occupancy_rt<256, true>(row_tiles) : occupancy_rt<256, false>(row_tiles);
+    case 512: return exact ? occupancy_rt<512, true>(row_tiles) : occupancy_rt<512, false>(row_tiles);
+    default: return 0;
+    }
+}
+
+}  // namespace dflash

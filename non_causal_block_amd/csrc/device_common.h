@@ -1,0 +1,184 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decomp.h"
+
+namespace dflash {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// 64-bit value broadcast/shift helpers built from 32-bit lane shuffles.
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int delta)
+{
+    int lo = __shfl_up((int)(uint32_t)(uint64_t)v, delta);
+    int hi = __shfl_up((int)(uint32_t)((uint64_t)v >> 32), delta);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+__device__ __forceinline__ int64_t shfl_i64(int64_t v, int src)
+{
+    int lo = __shfl((int)(uint32_t)(uint64_t)v, src);
+    int hi = __shfl((int)(uint32_t)((uint64_t)v >> 32), src);
+    return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int64_t t = shfl_up_i64(x, off);
+        if (lane >= off)
+            x += t;
+    }
+    return x;
+}
+
+// Work of request r (0 when r is out of range).
+__device__ __forceinline__ int64_t req_work_at(const int32_t* __restrict__ ctx_lens,
+                                               const int32_t* __restrict__ block_lens, int32_t r, const Decomp& d)
+{
+    if (r >= d.B)
+        return 0;
+    ReqGeom g = req_geom(ctx_lens[r], block_lens[r], d);
+    return req_work(g, d);
+}
+
+// Total tiles of the call; every lane of the wave gets the same value.
+__device__ __forceinline__ int64_t wave_total_work(const int32_t* __restrict__ ctx_lens,
+                                                   const int32_t* __restrict__ block_lens, const Decomp& d)
+{
+    const int lane = threadIdx.x & 63;
+    int64_t acc = 0;
+    for (int32_t base = 0; base < d.B; base += 64) {
+        int64_t w = req_work_at(ctx_lens, block_lens, base + lane, d);
+        acc += shfl_i64(wave_inclusive_scan(w), 63);
+    }
+    return acc;
+}
+
+// Request containing flat tile `pos` (0 <= pos < total) and the number of tiles
+// before it.  Requests with no work are skipped.  Wave-uniform result.
+__device__ __forceinline__ void wave_find_request(const int32_t* __restrict__ ctx_lens,
+                                                  const int32_t* __restrict__ block_lens, const Decomp& d,
+                                                  int64_t pos, int32_t& r_out, int64_t& base_out)
+{
+    const int lane = threadIdx.x & 63;
+    int64_t carry = 0;
+    for (int32_t base = 0; base < d.B; base += 64) {
+        int64_t w = req_work_at(ctx_lens, block_lens, base + lane, d);
+        int64_t incl = wave_inclusive_scan(w) + carry;
+        // first lane whose inclusive prefix exceeds pos
+        unsigned long long m = __ballot(incl > pos);
+        if (m) {
+            int src = __ffsll((long long)m) - 1;
+            r_out = base + src;
+            base_out = shfl_i64(incl - w, src);
+            return;
+        }
+        carry = shfl_i64(incl, 63);
+    }
+    r_out = d.B;  // not reached for pos < total
+    base_out = carry;
+}
+
+// Request owning packed query token t, with its first token index.  Wave-uniform.
+__device__ __forceinline__ void wave_find_token(const int32_t* __restrict__ block_lens, int32_t B, int64_t t,
+                                                int32_t& r_out, int64_t& qstart_out)
+{
+    const int lane = threadIdx.x & 63;
+    int64_t carry = 0;
+    for (int32_t base = 0; base < B; base += 64) {
+        int64_t n = (base + lane < B) ? (int64_t)block_lens[base + lane] : 0;
+        int64_t incl = wave_inclusive_scan(n) + carry;
+        unsigned long long m = __ballot(incl > t);
+        if (m) {
+            int src = __ffsll((long long)m) - 1;
+            r_out = base + src;
+            qstart_out = shfl_i64(incl - n, src);
+            return;
+        }
+        carry = shfl_i64(incl, 63);
+    }
+    r_out = B;
+    qstart_out = carry;
+}
+
+// Prefix of work over requests [0, r).  Wave-uniform.
+__device__ __forceinline__ int64_t wave_work_before(const int32_t* __restrict__ ctx_lens,
+                                                    const int32_t* __restrict__ block_lens, const Decomp& d, int32_t r)
+{
+    const int lane = threadIdx.x & 63;
+    int64_t acc = 0;
+    for (int32_t base = 0; base < r; base += 64) {
+        int64_t w = (base + lane < r) ? req_work_at(ctx_lens, block_lens, base + lane, d) : 0;
+        acc += shfl_i64(wave_inclusive_scan(w), 63);
+    }
+    return acc;
+}
+
+// Logical workgroup index: consecutive logical indices are placed on the same XCD
+// (the dispatcher deals workgroups round-robin over 8 XCDs), so the workgroups
+// that share a unit share that XCD's L2 for the unit's Q rows.
+__device__ __forceinline__ int32_t logical_wg(int32_t bid, int32_t P)
+{
+    constexpr int32_t kXcd = 8;
+    if (P % kXcd != 0)
+        return bid;
+    return (bid % kXcd) * (P / kXcd) + bid / kXcd;
+}
+
+// Kernel arguments shared by the attention kernels.
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k_pages;
+    const uint16_t* v_pages;
+    const int32_t* page_table;
+    const int32_t* ctx_lens;
+    const int32_t* block_lens;
+    const uint8_t* causal;
+    uint16_t* out;
+    float* part_o;     // [P][2][rmax][Dp]
+    float* part_lse;   // [P][2][rmax]
+    Decomp d;
+    int32_t Hq;
+    int32_t D;         // real head_dim
+    int32_t Dp;        // padded head_dim (partial row stride)
+    int32_t page_shift;
+    int32_t max_pages_per_req;
+    float scale_log2;  // scale * log2(e)
+};
+
+struct CombineArgs {
+    const int32_t* ctx_lens;
+    const int32_t* block_lens;
+    const float* part_o;
+    const float* part_lse;
+    uint16_t* out;
+    Decomp d;
+    int32_t Hq;
+    int32_t D;
+    int32_t Dp;
+    int64_t total_rows;  // total_q hint * Hq
+};
+
+}  // namespace dflash

@@ -1,0 +1,27 @@
+// kernels.h -- launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+
+namespace dflash {
+
+// Plain VALU kernel.
+hipError_t launch_attn_ref(const AttnArgs& a, hipStream_t stream);
+int ref_rows_per_unit();
+int ref_tile_keys();
+int ref_wgs_per_cu();  // resident workgroups per CU on the current device (0 if unknown)
+
+// MFMA kernel.  `row_tiles` is the number of 16-row MFMA tiles per unit
+// (rows per unit = 16 * row_tiles); `dpad` is 128, 256 or 512.
+hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
+int mfma_tile_keys();
+int mfma_max_row_tiles(int dpad);
+int mfma_wgs_per_cu(int dpad, int row_tiles, bool exact);  // on the current device (0 if unknown)
+
+// Split-KV combine.
+int combine_grid(int64_t total_rows);
+hipError_t launch_combine(const CombineArgs& a, int grid, hipStream_t stream);
+
+}  // namespace dflash

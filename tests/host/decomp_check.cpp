@@ -1,0 +1,133 @@
+// Host check of the work split in decomp.h (compiled with g++ by tests/test_decomp.py).
+//
+// Reads a case from stdin:  B Hkv G window rmax tk P  then B lines "L n".
+// Walks every workgroup's run exactly as the kernels do and checks that
+//   * every tile of every unit is processed by exactly one workgroup,
+//   * a unit handled whole by one workgroup is not also split,
+//   * the pieces of a split unit are exactly the (workgroup, slot) pairs the
+//     combine kernel derives from the unit's own tile range,
+//   * no slot of a workgroup is written twice.
+// Prints "OK <units> <split units> <max pieces>" or "FAIL <reason>".
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "decomp.h"
+
+using namespace dflash;
+
+int main()
+{
+    Decomp d;
+    if (scanf("%d %d %d %d %d %d %d", &d.B, &d.Hkv, &d.G, &d.window, &d.rmax, &d.tk, &d.P) != 7)
+        return 2;
+    std::vector<int> L(d.B), n(d.B);
+    for (int r = 0; r < d.B; ++r)
+        if (scanf("%d %d", &L[r], &n[r]) != 2)
+            return 2;
+    int64_t total = 0;
+    std::vector<int64_t> rbase(d.B + 1, 0);
+    for (int r = 0; r < d.B; ++r) {
+        ReqGeom g = req_geom(L[r], n[r], d);
+        rbase[r + 1] = rbase[r] + req_work(g, d);
+    }
+    total = rbase[d.B];
+    const int64_t tpw = tiles_per_wg(total, d.P);
+
+    // unit key -> list of (wg, slot, whole)
+    std::map<std::tuple<int, int, int>, std::vector<std::tuple<int64_t, int, bool>>> pieces;
+    std::vector<int> tile_hits(total, 0);
+    std::set<std::pair<int64_t, int>> slots_used;
+    for (int64_t wg = 0; wg < d.P; ++wg) {
+        const int64_t begin = wg * tpw;
+        const int64_t end = std::min<int64_t>(total, begin + tpw);
+        if (begin >= end)
+            continue;
+        int r = 0;
+        while (rbase[r + 1] <= begin)
+            ++r;
+        int64_t rb = rbase[r];
+        int64_t pos = begin;
+        int seg = 0;
+        while (pos < end) {
+            ReqGeom g = req_geom(L[r], n[r], d);
+            const int64_t w = req_work(g, d);
+            if (pos >= rb + w) {
+                rb += w;
+                ++r;
+                continue;
+            }
+            const int64_t off = pos - rb;
+            const int unit = (int)(off / g.ntiles);
+            const int t0 = (int)(off % g.ntiles);
+            const int64_t seg_end = std::min<int64_t>(end, rb + (int64_t)(unit + 1) * g.ntiles);
+            const int t1 = (int)(seg_end - rb - (int64_t)unit * g.ntiles);
+            const bool whole = t0 == 0 && t1 == g.ntiles;
+            const int slot = seg == 0 ? 0 : 1;
+            for (int64_t t = pos; t < seg_end; ++t)
+                tile_hits[t]++;
+            const int kvh = unit / g.ngroups, grp = unit % g.ngroups;
+            pieces[{r, kvh, grp}].push_back({wg, slot, whole});
+            if (!whole) {
+                if (!slots_used.insert({wg, slot}).second) {
+                    printf("FAIL slot written twice wg=%lld slot=%d\n", (long long)wg, slot);
+                    return 1;
+                }
+                // a partial piece must be the first or the last segment of the run
+                if (!(seg == 0 || seg_end == end)) {
+                    printf("FAIL partial segment in the middle of a run\n");
+                    return 1;
+                }
+            }
+            pos = seg_end;
+            ++seg;
+        }
+    }
+    for (int64_t t = 0; t < total; ++t)
+        if (tile_hits[t] != 1) {
+            printf("FAIL tile %lld hit %d times\n", (long long)t, tile_hits[t]);
+            return 1;
+        }
+    int split = 0;
+    size_t max_pieces = 0;
+    for (int r = 0; r < d.B; ++r) {
+        ReqGeom g = req_geom(L[r], n[r], d);
+        for (int kvh = 0; kvh < (g.ngroups ? d.Hkv : 0); ++kvh)
+            for (int grp = 0; grp < g.ngroups; ++grp) {
+                auto& pl = pieces[{r, kvh, grp}];
+                const int unit = kvh * g.ngroups + grp;
+                const int64_t us = rbase[r] + (int64_t)unit * g.ntiles;
+                const int64_t ue = us + g.ntiles;
+                const int64_t kf = us / tpw, kl = (ue - 1) / tpw;
+                if (kf == kl) {
+                    if (pl.size() != 1 || !std::get<2>(pl[0])) {
+                        printf("FAIL unit not whole in one workgroup\n");
+                        return 1;
+                    }
+                    continue;
+                }
+                ++split;
+                max_pieces = std::max(max_pieces, pl.size());
+                if ((int64_t)pl.size() != kl - kf + 1) {
+                    printf("FAIL split unit piece count\n");
+                    return 1;
+                }
+                for (int64_t k = kf; k <= kl; ++k) {
+                    const int slot = (k == kf && us != k * tpw) ? 1 : 0;  // the combine's rule
+                    bool found = false;
+                    for (auto& p : pl)
+                        if (std::get<0>(p) == k && std::get<1>(p) == slot && !std::get<2>(p))
+                            found = true;
+                    if (!found) {
+                        printf("FAIL combine cannot find piece wg=%lld slot=%d\n", (long long)k, slot);
+                        return 1;
+                    }
+                }
+            }
+    }
+    printf("OK %zu %d %zu\n", pieces.size(), split, max_pieces);
+    return 0;
+}

@@ -1,0 +1,174 @@
+"""The C ABI on the host: the library loads without a GPU, exports every
+symbol the header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import non_causal_block_amd as nb
+from non_causal_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash_block_attn.h")
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from non_causal_block_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dflash_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert nb.dflash_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert nb.dflash_status_string(s)
+    assert nb.dflash_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("hq,hkv,d,ok", [
+    (32, 8, 512, True), (32, 4, 512, True), (8, 2, 128, True), (32, 8, 256, True), (1, 1, 8, True),
+    (32, 8, 520, False), (32, 8, 100, False), (32, 7, 128, False), (0, 1, 128, False), (4, 8, 128, False),
+    (32, 8, 0, False),
+])
+def test_supports(lib, hq, hkv, d, ok):
+    assert nb.dflash_block_attn_supports(hq, hkv, d) == ok
+
+
+def desc(**kw):
+    base = dict(num_reqs=4, total_q=36, max_block_len=9, total_kv_len=82000, page_size=16,
+                max_pages_per_req=2100, num_pages=5200, num_cus=256)
+    base.update(kw)
+    return nb.make_desc(**base)
+
+
+def call(d, *, q=FAKE, k=FAKE, v=FAKE, pt=FAKE, ctx=FAKE, blk=FAKE, hq=32, hkv=4, hd=512, causal=None,
+         window=0, scale=0.044, out=FAKE):
+    return nb.dflash_block_attn(q, k, v, pt, ctx, blk, hq, hkv, hd, causal, window, scale, out, None, d)
+
+
+def expect(status, want, fragment=""):
+    assert status == want, (status, nb.dflash_last_error_message())
+    if fragment:
+        assert fragment in nb.dflash_last_error_message(), nb.dflash_last_error_message()
+
+
+def test_null_desc(lib):
+    st = lib.dflash_block_attn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4, 512, None, 0, 1.0, FAKE, None, None)
+    expect(st, nb.DFLASH_ERR_INVALID_ARGUMENT, "desc")
+
+
+def test_rejects_before_launch(lib):
+    d = desc()
+    expect(call(d, hd=520), nb.DFLASH_ERR_UNSUPPORTED, "512")
+    expect(call(d, hd=100), nb.DFLASH_ERR_UNSUPPORTED, "multiple of 8")
+    expect(call(d, hd=0), nb.DFLASH_ERR_INVALID_ARGUMENT)
+    expect(call(d, hq=30, hkv=4), nb.DFLASH_ERR_INVALID_ARGUMENT, "multiple")
+    expect(call(d, scale=math.inf), nb.DFLASH_ERR_INVALID_ARGUMENT, "scale")
+    expect(call(d, scale=math.nan), nb.DFLASH_ERR_INVALID_ARGUMENT, "scale")
+    expect(call(d, q=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    expect(call(d, out=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    expect(call(d, pt=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    expect(call(d, q=FAKE + 2), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    expect(call(d, ctx=FAKE + 1), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    # no workspace given
+    expect(call(d), nb.DFLASH_ERR_WORKSPACE_TOO_SMALL, "needs")
+    need = nb.dflash_block_attn_workspace_size(d, 32, 4, 512)
+    d.workspace = FAKE
+    d.workspace_bytes = need - 1
+    expect(call(d), nb.DFLASH_ERR_WORKSPACE_TOO_SMALL)
+    d.workspace = FAKE + 16
+    d.workspace_bytes = need
+    expect(call(d), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+
+
+@pytest.mark.parametrize("field,value", [
+    ("page_size", 0), ("page_size", 3), ("page_size", 2048), ("max_pages_per_req", 0), ("num_pages", 0),
+    ("kernel", 3), ("kernel", -1), ("num_workgroups", -1), ("num_cus", -2), ("num_reqs", -1), ("total_q", -5),
+])
+def test_rejects_bad_desc_fields(lib, field, value):
+    d = desc()
+    setattr(d, field, value)
+    expect(call(d), nb.DFLASH_ERR_INVALID_ARGUMENT)
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # nothing to do: OK without touching any pointer, workspace or device
+    assert call(desc(num_reqs=0), q=0, k=0, v=0, pt=0, ctx=0, blk=0, out=0) == nb.DFLASH_OK
+    assert call(desc(total_q=0), q=0, k=0, v=0, pt=0, ctx=0, blk=0, out=0) == nb.DFLASH_OK
+    assert nb.dflash_block_attn_workspace_size(desc(num_reqs=0), 32, 4, 512) == 0
+
+
+def test_plan_mfma_global_layer(lib):
+    # head_dim 512, 9 queries x 8 q-heads per kv-head = 72 rows -> five 16-row tiles
+    p = nb.dflash_block_attn_plan(desc(), 32, 4, 512)
+    assert p.kernel == nb.DFLASH_KERNEL_MFMA
+    assert p.rows_per_unit == 80 and p.head_dim_padded == 512 and p.tile_keys == 32
+    assert p.num_workgroups == 256  # planning without a device assumes one workgroup per CU
+    assert p.workspace_bytes >= p.num_workgroups * 2 * 80 * 512 * 4 + p.num_workgroups * 2 * 80 * 4
+    assert p.combine_workgroups == (36 * 32 + 3) // 4
+
+
+def test_plan_small_problem_uses_few_workgroups(lib):
+    d = desc(num_reqs=1, total_q=9, total_kv_len=521, max_pages_per_req=33, num_pages=34)
+    p = nb.dflash_block_attn_plan(d, 8, 2, 128)
+    # 17 tiles per kv-head, two kv-heads: a handful of workgroups, not the whole chip
+    assert 1 <= p.num_workgroups <= 8
+    assert p.head_dim_padded == 128 and p.rows_per_unit == 48
+
+
+def test_plan_reference_kernel_and_forced_grid(lib):
+    p = nb.dflash_block_attn_plan(desc(kernel=nb.DFLASH_KERNEL_REFERENCE, num_workgroups=37), 32, 4, 200)
+    assert p.kernel == nb.DFLASH_KERNEL_REFERENCE and p.num_workgroups == 37
+    assert p.rows_per_unit == 16 and p.head_dim_padded == 200
+    p1 = nb.dflash_block_attn_plan(desc(num_workgroups=1), 32, 4, 512)
+    assert p1.workspace_bytes == 0 and p1.combine_workgroups == 0
+
+
+def test_plan_head_dim_padding(lib):
+    for hd, want in ((8, 128), (64, 128), (136, 256), (256, 256), (264, 512), (512, 512)):
+        assert nb.dflash_block_attn_plan(desc(), 32, 4, hd).head_dim_padded == want
+
+
+def test_workspace_size_matches_plan(lib):
+    d = desc(max_block_len=16)
+    assert nb.dflash_block_attn_workspace_size(d, 32, 8, 256) == nb.dflash_block_attn_plan(d, 32, 8, 256).workspace_bytes
+
+
+def test_planning_without_device_needs_cu_count(lib):
+    # with num_cus = 0 the planner must ask the HIP runtime for the device; on a host
+    # without a GPU that is a clean error, not a crash
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(nb.DFlashError) as e:
+        nb.dflash_block_attn_plan(desc(num_cus=0), 32, 4, 512)
+    assert e.value.status == nb.DFLASH_ERR_HIP
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(OSError):
+        _lib.load()

@@ -1,0 +1,257 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs an MI355X).
+
+Every call goes through the C ABI (non_causal_block_amd -> libdflash_attn.so).
+Tolerances: max|err| <= 2e-2 and mean|err| <= 2e-3 on bf16 outputs, plus a
+relative RMS error <= 1e-2 (tests/gpu_helpers.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import non_causal_block_amd as nb
+import oracle
+import workloads
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = [("mfma", nb.DFLASH_KERNEL_MFMA), ("ref", nb.DFLASH_KERNEL_REFERENCE)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+
+
+def _full(name, kernel, **kw):
+    wl = workloads.make(name, **kw)
+    ref = oracle.run_workload(wl)
+    got = H.to_f64(H.run(wl, kernel=kernel))
+    return H.assert_parity(got, ref, f"{name} kernel={kernel}")
+
+
+# ---------------------------------------------------------------------------
+# the five configurations
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_c1_tiny_d128(kname, kernel):
+    _full("c1_tiny_d128", kernel)
+
+
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_c2_paged_d256(kname, kernel):
+    _full("c2_paged_d256", kernel)
+
+
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_c3_global_d512(kname, kernel):
+    _full("c3_global_d512", kernel)
+
+
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_c4_causal_window_d256(kname, kernel):
+    _full("c4_causal_window_d256", kernel)
+
+
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_c5_mixed_d512_reduced(kname, kernel):
+    _full("c5_mixed_d512", kernel, ctx_cap=1500)
+
+
+def test_c5_mixed_d512_full_sampled():
+    """Full-size mixed batch in the benchmark's launch configuration; the oracle
+    computes a sample of rows: every row of the longest request, of a causal and of
+    the shortest request, and random rows elsewhere."""
+    wl = workloads.make("c5_mixed_d512")
+    out = H.to_f64(H.run(wl)).reshape(-1, wl.D)
+    qs = wl.q_start
+    pick = set()
+    for r in (int(np.argmax(wl.ctx_lens)), int(np.argmin(wl.ctx_lens)), int(np.flatnonzero(wl.causal)[0])):
+        for t in range(qs[r], qs[r + 1]):
+            pick.update(range(t * wl.Hq, (t + 1) * wl.Hq))
+    rng = np.random.default_rng(0)
+    pick.update(rng.choice(wl.total_q * wl.Hq, size=400, replace=False).tolist())
+    rows = np.array(sorted(pick), dtype=np.int64)
+    ref = oracle.run_workload(wl, rows=rows)
+    H.assert_parity(out[rows], ref, "c5 full sampled")
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+EDGE = [
+    # (Hq, Hkv, D, ctx_lens, block_lens, causal, window, page_size)
+    (4, 1, 128, [0, 1, 15, 16, 17, 31, 32, 33], [1, 2, 9, 16, 1, 2, 9, 16], [0, 1, 0, 1, 0, 1, 0, 1], 0, 16),
+    (8, 8, 256, [0, 5, 40], [3, 0, 7], [1, 0, 1], 0, 16),          # Hq == Hkv, an empty block
+    (32, 4, 512, [100, 63, 64], [16, 9, 1], [0, 1, 0], 0, 16),     # 128 rows: two row groups
+    (16, 2, 64, [70, 3], [5, 4], [1, 0], 0, 16),                   # head_dim 64 (padded)
+    (16, 2, 136, [70, 3], [5, 4], [1, 0], 0, 16),                  # head_dim 136 (padded)
+    (16, 4, 264, [130, 9], [9, 16], [0, 1], 0, 16),                # head_dim 264 (padded 512)
+    (8, 2, 128, [50, 200, 7], [9, 5, 4], [1, 1, 0], 1, 16),        # window 1: only itself
+    (8, 2, 128, [50, 200, 7], [9, 5, 4], [1, 0, 1], 2, 16),
+    (8, 2, 128, [50, 200, 7], [9, 5, 4], [1, 0, 1], 16, 16),
+    (8, 2, 128, [50, 200, 7], [9, 5, 4], [0, 0, 0], 17, 16),       # non-causal + window
+    (8, 2, 128, [50, 200, 7], [9, 5, 4], [1, 1, 1], 300, 16),      # window wider than the context
+    (8, 2, 256, [333, 77], [9, 9], [0, 1], 0, 8),                  # page size 8
+    (8, 2, 256, [333, 77], [9, 9], [0, 1], 40, 32),                # page size 32
+    (8, 2, 128, [0], [1], [0], 0, 16),                             # a single key
+    (12, 3, 128, [1000, 2, 515], [15, 16, 9], [1, 0, 1], 100, 16),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_edges(case, kname, kernel):
+    Hq, Hkv, D, L, n, c, W, P = EDGE[case]
+    wl = workloads.build(len(L), Hq, Hkv, D, L, n, c, window=W, seed=100 + case, page_size=P, extra_pages=2)
+    ref = oracle.run_workload(wl)
+    for nwg in (0, 1, 5):
+        got = H.to_f64(H.run(wl, kernel=kernel, num_workgroups=nwg))
+        H.assert_parity(got, ref, f"edge {case} kernel={kname} wg={nwg}")
+
+
+def test_causal_null_means_all_noncausal():
+    wl = workloads.build(3, 8, 2, 128, [40, 9, 100], [9, 4, 9], [0, 0, 0], seed=5)
+    ref = oracle.run_workload(wl)
+    got = H.to_f64(H.run(wl, causal_none=True))
+    H.assert_parity(got, ref, "causal=NULL")
+
+
+def test_no_hints():
+    wl = workloads.make("c2_paged_d256", ctx_cap=900)
+    ref = oracle.run_workload(wl)
+    H.assert_parity(H.to_f64(H.run(wl, hints=False)), ref, "no hints")
+
+
+# ---------------------------------------------------------------------------
+# key-set membership: a dominant key planted at each mask edge
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_spike_at_mask_edges(kname, kernel):
+    """Query i's logit for one key is made huge.  If the key is visible the output is
+    that key's value row; if not, the output ignores it.  Keys probed: the block's
+    own i and i+1 (causal edge), and the window edges lo-1 and lo."""
+    Hq, Hkv, D, L, n, W = 4, 1, 128, 70, 6, 9
+    for causal in (0, 1):
+        for target_rel in ("self", "next", "lo", "lo-1"):
+            rng = np.random.default_rng(11)
+            wl = workloads.build(1, Hq, Hkv, D, [L], [n], [causal], window=W, seed=3)
+            k = workloads.bf16_bits_to_f32(wl.k).astype(np.float32) * 0.05
+            q = np.zeros((n, Hq, D), np.float32)
+            for i in range(n):
+                p = L + i
+                tgt = {"self": p, "next": p + 1, "lo": p - W + 1, "lo-1": p - W}[target_rel]
+                if not (0 <= tgt < L + n):
+                    continue
+                # one distinct direction per query position
+                dirv = np.zeros(D, np.float32)
+                dirv[i % D] = 1.0
+                k[tgt, 0] += 4.0 * dirv
+                q[i, :, :] = 30.0 * dirv
+            wl.k = workloads.f32_to_bf16_bits(k)
+            wl.q = workloads.f32_to_bf16_bits(q)
+            wl.k_pages = workloads.scatter_to_pages(wl.k, wl.kv_lens, wl.page_table, wl.num_pages, wl.page_size, True)
+            ref = oracle.run_workload(wl)
+            got = H.to_f64(H.run(wl, kernel=kernel))
+            H.assert_parity(got, ref, f"spike causal={causal} target={target_rel}")
+
+
+def test_extreme_logit_range_recomputes_exactly():
+    """Logits that climb by far more than 2^32 along the context: the lazy reference
+    is abandoned and the segment recomputed with the exact row max."""
+    Hq, Hkv, D = 4, 1, 128
+    for L in (40, 700, 3000):
+        wl = workloads.build(2, Hq, Hkv, D, [L, 33], [9, 5], [0, 1], seed=21)
+        k = workloads.bf16_bits_to_f32(wl.k).astype(np.float32)
+        # key norms grow along the sequence: later tiles have much larger logits
+        ramp = np.linspace(0.0, 60.0, k.shape[0], dtype=np.float32)
+        k[:, 0, 0] = ramp
+        q = workloads.bf16_bits_to_f32(wl.q).astype(np.float32)
+        q[:, :, 0] = 8.0
+        wl.k = workloads.f32_to_bf16_bits(k)
+        wl.q = workloads.f32_to_bf16_bits(q)
+        wl.k_pages = workloads.scatter_to_pages(wl.k, wl.kv_lens, wl.page_table, wl.num_pages, wl.page_size, True)
+        ref = oracle.run_workload(wl)
+        for nwg in (0, 1, 3):
+            got = H.to_f64(H.run(wl, num_workgroups=nwg))
+            H.assert_parity(got, ref, f"extreme L={L} wg={nwg}")
+
+
+# ---------------------------------------------------------------------------
+# properties of the GPU path itself
+# ---------------------------------------------------------------------------
+def test_split_invariance():
+    wl = workloads.make("c3_global_d512", ctx_cap=4000)
+    t = H.upload(wl)
+    base = H.to_f64(H.run(wl, t, num_workgroups=1))
+    for nwg in (2, 3, 7, 64, 256, 1000):
+        got = H.to_f64(H.run(wl, t, num_workgroups=nwg))
+        # different split points change fp32 rounding only: within two bf16 ulps
+        assert np.all(np.abs(got - base) <= 2 * 2.0 ** -8 * np.abs(base) + 1e-6), nwg
+
+
+def test_page_permutation_invariance_is_bitwise():
+    a = workloads.make("c2_paged_d256", ctx_cap=1200)
+    b = workloads.build(a.B, a.Hq, a.Hkv, a.D, a.ctx_lens, a.block_lens, a.causal, seed=999, extra_pages=5)
+    # same logical data, different physical pages
+    b.q, b.k, b.v = a.q, a.k, a.v
+    b.k_pages = workloads.scatter_to_pages(b.k, b.kv_lens, b.page_table, b.num_pages, b.page_size, True)
+    b.v_pages = workloads.scatter_to_pages(b.v, b.kv_lens, b.page_table, b.num_pages, b.page_size, True)
+    oa = H.run(a).cpu()
+    ob = H.run(b).cpu()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_determinism_is_bitwise():
+    wl = workloads.make("c4_causal_window_d256")
+    t = H.upload(wl)
+    o1 = H.run(wl, t).cpu()
+    o2 = H.run(wl, t).cpu()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_poison_and_guard_bands():
+    """NaN page tails and unused pages never reach the output; rows of `out`
+    outside the call's range are never written."""
+    wl = workloads.make("c5_mixed_d512", ctx_cap=700, B=12)   # pages are NaN-poisoned
+    ref = oracle.run_workload(wl)
+    t = H.upload(wl)
+    guard = 7
+    big = torch.full((wl.total_q + 2 * guard, wl.Hq, wl.D), 3.0, dtype=torch.bfloat16, device=H.dev())
+    inner = big[guard:guard + wl.total_q]
+    H.run(wl, t, out=inner)
+    got = H.to_f64(inner)
+    H.assert_parity(got, ref, "poison")
+    assert torch.all(big[:guard] == 3.0) and torch.all(big[guard + wl.total_q:] == 3.0)
+
+
+def test_timing_events_are_recorded():
+    wl = workloads.make("c1_tiny_d128")
+    t = H.upload(wl)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    d = nb.make_desc(num_reqs=wl.B, total_q=wl.total_q, max_block_len=9, total_kv_len=wl.total_kv,
+                     page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req, num_pages=wl.num_pages)
+    need = nb.dflash_block_attn_workspace_size(d, wl.Hq, wl.Hkv, wl.D)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=H.dev())
+    d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    d.event_attn_begin, d.event_attn_end = ev0.cuda_event, ev1.cuda_event
+    out = torch.empty((wl.total_q, wl.Hq, wl.D), dtype=torch.bfloat16, device=H.dev())
+    st = nb.dflash_block_attn(t["q"], t["k"], t["v"], t["pt"], t["ctx"], t["blk"], wl.Hq, wl.Hkv, wl.D, t["causal"],
+                              wl.window, wl.scale, out, torch.cuda.current_stream().cuda_stream, d)
+    assert st == nb.DFLASH_OK, nb.dflash_last_error_message()
+    torch.cuda.synchronize()
+    assert ev0.elapsed_time(ev1) > 0
+    H.assert_parity(H.to_f64(out), oracle.run_workload(wl), "events")
+
+
+def test_plan_on_device():
+    wl = workloads.make("c3_global_d512")
+    d = nb.make_desc(num_reqs=wl.B, total_q=wl.total_q, max_block_len=9, total_kv_len=wl.total_kv,
+                     page_size=16, max_pages_per_req=wl.max_pages_per_req, num_pages=wl.num_pages)
+    p = nb.dflash_block_attn_plan(d, wl.Hq, wl.Hkv, wl.D)
+    props = torch.cuda.get_device_properties(0)
+    assert p.kernel == nb.DFLASH_KERNEL_MFMA and p.rows_per_unit == 80
+    assert p.num_workgroups % props.multi_processor_count == 0
