@@ -45,6 +45,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -62,6 +63,22 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
 __device__ __forceinline__ u32x4_t ldg16(const uint16_t* p)
 {
     return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// K/V rows are read once per call: a streaming (nontemporal) load does not
+// allocate them in the caches, which keeps the last-level cache from evicting
+// (and writing back) other data on their account.
+__device__ __forceinline__ u32x4_t ldg16_stream(const uint16_t* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane 4q+r
+// receives element r of the 8-byte rows addressed by lanes q, q+4, q+8, q+12.
+__device__ __forceinline__ u32x2_t ds_read_tr16(const unsigned char* p)
+{
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+    return __builtin_bit_cast(u32x2_t, v);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -82,9 +99,16 @@ struct Cfg {
     // With head_dim 512 and 4-5 row tiles the Q^T operands live in LDS, not registers:
     // the register file cannot hold them next to the 128-160 accumulators.
     static constexpr bool QLDS = DP == 512 && RT >= 4;
-    // V tile, row-major [key][d_local]; transposed reads walk down a column and the
-    // 8-byte row pad spreads the four lane groups over different banks
-    static constexpr int VROW = DW * 2 + 8;
+    // V tile, row-major [key][d_local], addressed in 8-byte chunks.  A transposing
+    // read touches four key rows of 32 bytes per 16-lane group (eight rows per
+    // 32-lane pass).  Rows of 256 bytes XOR the chunk index with 4*(row % 8), which
+    // puts the eight rows of a pass on distinct banks; shorter rows get a 32-byte pad.
+    static constexpr bool VSWZ = DW * 2 == 256;
+    static constexpr int VROW = VSWZ ? DW * 2 : DW * 2 + 32;
+    static __device__ __forceinline__ int vofs(int row, int chunk)
+    {
+        return row * VROW + 8 * (VSWZ ? chunk ^ ((row & 7) << 2) : chunk);
+    }
     // LDS layout (bytes)
     static constexpr int SX_BYTES = kWaves * 2 * RT * 64 * 16;  // partial S^T [wave][h][b][lane]
     static constexpr int PX_BYTES = RT * 64 * 16;               // P^T (B operand) [b][lane]
@@ -243,13 +267,21 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
             // stays in bounds; their V is zeroed and their logits are masked.
             const int64_t safe_row =
                 ((int64_t)pt[g.kv_lo >> a.page_shift] * psize + (g.kv_lo & (psize - 1))) * d.Hkv * (int64_t)D;
-            auto key_row = [&](int32_t t, int h, bool& valid) -> int64_t {
+            // A tile key is located in two steps so that no wait lands on loads in flight:
+            // key_page() reads the page-table entry (at a clamped, always valid index) one
+            // tile ahead; key_row() turns it into a row offset only when the tile's K/V
+            // are requested.  Keys past the end use the request's first key row so that
+            // every load stays in bounds; their V is zeroed and their logits are masked.
+            auto key_page = [&](int32_t t, int h) -> int32_t {
+                const int32_t key = g.kv_lo + t * kTK + 16 * h + l16;
+                const int32_t kc = key < T ? key : T - 1;
+                return pt[kc >> a.page_shift];
+            };
+            auto key_row = [&](int32_t t, int h, int32_t page, bool& valid) -> int64_t {
                 const int32_t key = g.kv_lo + t * kTK + 16 * h + l16;
                 valid = key < T;
-                if (!valid)
-                    return safe_row;
-                const int64_t page = pt[key >> a.page_shift];
-                return (page * psize + (key & (psize - 1))) * d.Hkv * (int64_t)D;
+                const int64_t row = ((int64_t)page * psize + (key & (psize - 1))) * d.Hkv * (int64_t)D;
+                return valid ? row : safe_row;
             };
 
             float m_fix[NOWN];
@@ -275,8 +307,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                 }
                 bool aborted = false;
 
-                int64_t krow[2], krow_next[2];
-                bool kval[2], kval_next[2];
+                int64_t krow[2];
+                int32_t kpage_next[2];
+                bool kval[2];
                 u32x4_t kr[2][KS], vr[2][KS];
                 auto issue_kv = [&]() {
 #pragma unroll
@@ -286,9 +319,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
                         for (int s = 0; s < KS; ++s) {
                             const int e = (EXACT || dval[s]) ? wbase + 32 * s + 8 * grp4 : 0;
-                            kr[h][s] = ldg16(kp + e);
+                            kr[h][s] = ldg16_stream(kp + e);
                             if constexpr (MODE != kMaxScan)
-                                vr[h][s] = ldg16(vp + e);
+                                vr[h][s] = ldg16_stream(vp + e);
                         }
                     }
                 };
@@ -296,14 +329,17 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                 // One 32-key tile per step: the registers of tile t are consumed first (V
                 // into LDS, K into the S^T MFMAs); then tile t+1 is requested into the same
                 // registers, so its loads overlap the softmax and PV product of tile t.
-                krow[0] = key_row(t0, 0, kval[0]);
-                krow[1] = key_row(t0, 1, kval[1]);
-                issue_kv();
+                krow[0] = key_row(t0, 0, key_page(t0, 0), kval[0]);
+                krow[1] = key_row(t0, 1, key_page(t0, 1), kval[1]);
                 if (t0 + 1 < t1) {
-                    krow_next[0] = key_row(t0 + 1, 0, kval_next[0]);
-                    krow_next[1] = key_row(t0 + 1, 1, kval_next[1]);
+                    kpage_next[0] = key_page(t0 + 1, 0);
+                    kpage_next[1] = key_page(t0 + 1, 1);
                 }
-                for (int32_t t = t0; t < t1; ++t) {
+                issue_kv();
+                // An abandoned lazy segment leaves by the loop condition only: an exit between
+                // the softmax and the PV product would make the compiler keep a second copy of
+                // every accumulator.  The tile that triggered it still runs its (discarded) PV.
+                for (int32_t t = t0; t < t1 && !aborted; ++t) {
                     const int32_t k0 = g.kv_lo + t * kTK;
                     // (1) this wave's V slice -> LDS [key][d_local]; absent keys/d are zero
                     if constexpr (MODE != kMaxScan) {
@@ -312,46 +348,54 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
                             for (int s = 0; s < KS; ++s) {
                                 const bool keep = kval[h] && dval[s];
-                                const u32x2_t lo2 = {keep ? vr[h][s][0] : 0u, keep ? vr[h][s][1] : 0u};
-                                const u32x2_t hi2 = {keep ? vr[h][s][2] : 0u, keep ? vr[h][s][3] : 0u};
-                                unsigned char* dst = vls + (16 * h + l16) * C::VROW + (32 * s + 8 * grp4) * 2;
-                                *reinterpret_cast<u32x2_t*>(dst) = lo2;
-                                *reinterpret_cast<u32x2_t*>(dst + 8) = hi2;
+                                u32x4_t x = vr[h][s];
+                                x[0] = keep ? x[0] : 0u;
+                                x[1] = keep ? x[1] : 0u;
+                                x[2] = keep ? x[2] : 0u;
+                                x[3] = keep ? x[3] : 0u;
+                                *reinterpret_cast<u32x4_t*>(vls + C::vofs(16 * h + l16, 8 * s + 2 * grp4)) = x;
                             }
                     }
                     // (2) partial S^T over this wave's d-slice (absent d: Q is zero there;
                     //     absent keys are masked below, whatever their K holds)
+                    bf16x8_t kb[2][KS];
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int b = 0; b < RT; ++b) {
-                            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                        for (int s = 0; s < KS; ++s) {
+                            u32x4_t kx = kr[h][s];
+                            kx[0] = dval[s] ? kx[0] : 0u;
+                            kx[1] = dval[s] ? kx[1] : 0u;
+                            kx[2] = dval[s] ? kx[2] : 0u;
+                            kx[3] = dval[s] ? kx[3] : 0u;
+                            kb[h][s] = as_bf16x8(kx);
+                        }
 #pragma unroll
-                            for (int s = 0; s < KS; ++s) {
-                                u32x4_t kx = kr[h][s];
-                                kx[0] = dval[s] ? kx[0] : 0u;
-                                kx[1] = dval[s] ? kx[1] : 0u;
-                                kx[2] = dval[s] ? kx[2] : 0u;
-                                kx[3] = dval[s] ? kx[3] : 0u;
-                                if constexpr (C::QLDS)
-                                    acc = mfma16(as_bf16x8(kx), as_bf16x8(qls[(b * KS + s) * kThreads + threadIdx.x]),
-                                                 acc);
-                                else
-                                    acc = mfma16(as_bf16x8(kx), qf[b][s], acc);
-                            }
-                            sx[((wave * 2 + h) * RT + b) * 64 + lane] = acc;
+                    for (int b = 0; b < RT; ++b) {
+                        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < KS; ++s) {
+                            bf16x8_t qb;
+                            if constexpr (C::QLDS)
+                                qb = as_bf16x8(qls[(b * KS + s) * kThreads + threadIdx.x]);
+                            else
+                                qb = qf[b][s];
+                            acc0 = mfma16(kb[0][s], qb, acc0);
+                            acc1 = mfma16(kb[1][s], qb, acc1);
                         }
-                    // request tile t+1 (registers are free now), then the page entries of t+2
+                        sx[((wave * 2 + 0) * RT + b) * 64 + lane] = acc0;
+                        sx[((wave * 2 + 1) * RT + b) * 64 + lane] = acc1;
+                    }
+                    // request tile t+1 (registers are free now); the page entries of t+2 first,
+                    // so that waiting for them later never waits for the K/V of t+1
                     if (t + 1 < t1) {
-                        krow[0] = krow_next[0];
-                        krow[1] = krow_next[1];
-                        kval[0] = kval_next[0];
-                        kval[1] = kval_next[1];
-                        issue_kv();
+                        krow[0] = key_row(t + 1, 0, kpage_next[0], kval[0]);
+                        krow[1] = key_row(t + 1, 1, kpage_next[1], kval[1]);
                         if (t + 2 < t1) {
-                            krow_next[0] = key_row(t + 2, 0, kval_next[0]);
-                            krow_next[1] = key_row(t + 2, 1, kval_next[1]);
+                            kpage_next[0] = key_page(t + 2, 0);
+                            kpage_next[1] = key_page(t + 2, 1);
                         }
+                        issue_kv();
                     }
                     __syncthreads();
                     // (3) owners: reduce, mask, softmax, publish P^T
@@ -431,28 +475,27 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
                         for (int b = 0; b < RT; ++b)
                             anyover |= flag_s[b];
-                        if (anyover) {
-                            aborted = true;
-                            break;
-                        }
+                        aborted = anyover != 0;
                     }
                     // (4) O^T += V^T P^T for this wave's d-slice
+                    // A operand V^T: lane l holds d = 16c + l%16 at key slots 4*grp4 + 0..3
+                    // and 16 + 4*grp4 + 0..3 (the key order of P^T).  Transposing reads:
+                    // lane j of group grp4 addresses key 4*grp4 + j/4 (and +16) at
+                    // d = 16c + 4*(j%4).  All reads are issued before the first product.
                     bf16x8_t pb[RT];
 #pragma unroll
                     for (int b = 0; b < RT; ++b)
                         pb[b] = as_bf16x8(px[b * 64 + lane]);
+                    const int vrow = 4 * grp4 + (l16 >> 2);
+                    u32x2_t vt[DT][2];
 #pragma unroll
                     for (int c = 0; c < DT; ++c) {
-                        // A operand: V^T rows d = 16c + l16; key slots 4*grp4 + 0..3, 16 + 4*grp4 + 0..3
-                        const unsigned char* col = vls + (16 * c + l16) * 2;
-                        u32x4_t va;
+                        vt[c][0] = ds_read_tr16(vls + C::vofs(vrow, 4 * c + (l16 & 3)));
+                        vt[c][1] = ds_read_tr16(vls + C::vofs(vrow + 16, 4 * c + (l16 & 3)));
+                    }
 #pragma unroll
-                        for (int e2 = 0; e2 < 4; ++e2) {
-                            const int k0e = (e2 < 2) ? (4 * grp4 + 2 * e2) : (16 + 4 * grp4 + 2 * (e2 - 2));
-                            const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(col + k0e * C::VROW);
-                            const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(col + (k0e + 1) * C::VROW);
-                            va[e2] = lo16 | (hi16 << 16);
-                        }
+                    for (int c = 0; c < DT; ++c) {
+                        const u32x4_t va = {vt[c][0][0], vt[c][0][1], vt[c][1][0], vt[c][1][1]};
                         const bf16x8_t vb = as_bf16x8(va);
 #pragma unroll
                         for (int b = 0; b < RT; ++b)

@@ -55,37 +55,73 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     if (kf == kl)
         return;  // finished inside one workgroup, already written
 
+    // piece weights, lane-parallel: lane j holds piece kf + j (+ 64 per round)
+    const int64_t npieces = kl - kf + 1;
     float M = -INFINITY;
-    for (int64_t k = kf; k <= kl; ++k) {
-        const int slot = (k == kf && us != k * tpw) ? 1 : 0;
-        M = fmaxf(M, a.part_lse[(k * 2 + slot) * d.rmax + rin]);
+    for (int64_t base = 0; base < npieces; base += 64) {
+        const int64_t k = kf + base + lane;
+        if (k <= kl) {
+            const int slot = (k == kf && us != k * tpw) ? 1 : 0;
+            M = fmaxf(M, a.part_lse[(k * 2 + slot) * d.rmax + rin]);
+        }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        M = fmaxf(M, __shfl_xor(M, off));
+
     const int32_t d0 = lane * 8;
+    const bool dlive = d0 < a.D;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         acc[e] = 0.f;
     float W = 0.f;
-    for (int64_t k = kf; k <= kl; ++k) {
-        const int slot = (k == kf && us != k * tpw) ? 1 : 0;
-        const int64_t prow = (k * 2 + slot) * d.rmax + rin;
-        const float lse = a.part_lse[prow];
-        const float w = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
-        W += w;
-        if (d0 < a.D && w != 0.f) {
-            const float4* src = reinterpret_cast<const float4*>(a.part_o + prow * a.Dp + d0);
-            const float4 x0 = src[0];
-            const float4 x1 = src[1];
-            acc[0] = fmaf(w, x0.x, acc[0]);
-            acc[1] = fmaf(w, x0.y, acc[1]);
-            acc[2] = fmaf(w, x0.z, acc[2]);
-            acc[3] = fmaf(w, x0.w, acc[3]);
-            acc[4] = fmaf(w, x1.x, acc[4]);
-            acc[5] = fmaf(w, x1.y, acc[5]);
-            acc[6] = fmaf(w, x1.z, acc[6]);
-            acc[7] = fmaf(w, x1.w, acc[7]);
+    for (int64_t base = 0; base < npieces; base += 64) {
+        const int64_t kq = kf + base + lane;
+        float wl = 0.f;
+        if (kq <= kl) {
+            const int slot = (kq == kf && us != kq * tpw) ? 1 : 0;
+            const float lse = a.part_lse[(kq * 2 + slot) * d.rmax + rin];
+            wl = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
+        }
+        W += wl;
+        const int cnt = (int)min<int64_t>(64, npieces - base);
+        // four pieces per step keep eight 16-byte loads of each lane in flight
+        for (int j0 = 0; j0 < cnt; j0 += 4) {
+            float wj[4];
+            float4 x0[4], x1[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = min(j0 + u, cnt - 1);
+                wj[u] = (j0 + u < cnt) ? __shfl(wl, j) : 0.f;
+                const int64_t k = kf + base + j;
+                const int slot = (k == kf && us != k * tpw) ? 1 : 0;
+                const int64_t prow = (k * 2 + slot) * d.rmax + rin;
+                if (dlive && wj[u] != 0.f) {
+                    const float4* src = reinterpret_cast<const float4*>(a.part_o + prow * a.Dp + d0);
+                    x0[u] = src[0];
+                    x1[u] = src[1];
+                } else {
+                    x0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    x1[u] = x0[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc[0] = fmaf(wj[u], x0[u].x, acc[0]);
+                acc[1] = fmaf(wj[u], x0[u].y, acc[1]);
+                acc[2] = fmaf(wj[u], x0[u].z, acc[2]);
+                acc[3] = fmaf(wj[u], x0[u].w, acc[3]);
+                acc[4] = fmaf(wj[u], x1[u].x, acc[4]);
+                acc[5] = fmaf(wj[u], x1[u].y, acc[5]);
+                acc[6] = fmaf(wj[u], x1[u].z, acc[6]);
+                acc[7] = fmaf(wj[u], x1[u].w, acc[7]);
+            }
         }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        W += __shfl_xor(W, off);
     if (d0 < a.D) {
         const float inv = W > 0.f ? 1.f / W : 0.f;
         uint16_t* dst = a.out + (t * a.Hq + h) * (int64_t)a.D + d0;

@@ -166,7 +166,7 @@ def test_extreme_logit_range_recomputes_exactly():
         wl = workloads.build(2, Hq, Hkv, D, [L, 33], [9, 5], [0, 1], seed=21)
         k = workloads.bf16_bits_to_f32(wl.k).astype(np.float32)
         # key norms grow along the sequence: later tiles have much larger logits
-        ramp = np.linspace(0.0, 60.0, k.shape[0], dtype=np.float32)
+        ramp = np.linspace(0.0, 200.0, k.shape[0], dtype=np.float32)
         k[:, 0, 0] = ramp
         q = workloads.bf16_bits_to_f32(wl.q).astype(np.float32)
         q[:, :, 0] = 8.0
@@ -183,13 +183,26 @@ def test_extreme_logit_range_recomputes_exactly():
 # properties of the GPU path itself
 # ---------------------------------------------------------------------------
 def test_split_invariance():
+    """Any split of the key ranges over workgroups gives the oracle's result, and the
+    splits agree with each other far more tightly than the parity bound: each piece
+    rounds its probabilities to bf16 relative to its own reference max, so outputs
+    may differ by a few bf16 ulps, nothing more."""
     wl = workloads.make("c3_global_d512", ctx_cap=4000)
+    ref = oracle.run_workload(wl)
     t = H.upload(wl)
     base = H.to_f64(H.run(wl, t, num_workgroups=1))
+    H.assert_parity(base, ref, "split 1")
+    scale = float(np.sqrt(np.mean(base * base)))
     for nwg in (2, 3, 7, 64, 256, 1000):
         got = H.to_f64(H.run(wl, t, num_workgroups=nwg))
-        # different split points change fp32 rounding only: within two bf16 ulps
-        assert np.all(np.abs(got - base) <= 2 * 2.0 ** -8 * np.abs(base) + 1e-6), nwg
+        H.assert_parity(got, ref, f"split {nwg}")
+        diff = np.abs(got - base)
+        # a dominant key's probability rounded to bf16 (2^-9 relative) moves an output
+        # by up to ~2^-9 * max|v|; allow that, far below the 2e-2 parity bound
+        # two independent bf16 roundings alone differ by ~2^-9 relative rms
+        rel = float(np.sqrt(np.mean(diff * diff))) / scale
+        assert rel <= 5e-3, (nwg, rel)
+        assert float(np.max(diff)) <= 4e-3, (nwg, float(np.max(diff)))
 
 
 def test_page_permutation_invariance_is_bitwise():
@@ -232,6 +245,10 @@ def test_timing_events_are_recorded():
     t = H.upload(wl)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()  # torch creates the HIP event on first record
+    ev1.record()
+    torch.cuda.synchronize()
+    assert ev0.cuda_event and ev1.cuda_event
     d = nb.make_desc(num_reqs=wl.B, total_q=wl.total_q, max_block_len=9, total_kv_len=wl.total_kv,
                      page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req, num_pages=wl.num_pages)
     need = nb.dflash_block_attn_workspace_size(d, wl.Hq, wl.Hkv, wl.D)
