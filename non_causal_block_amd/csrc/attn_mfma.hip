@@ -30,8 +30,9 @@
 //    workgroup recomputes such segments with each row's exact max found by a
 //    K-only pass.  Numerator and denominator share the reference, so the
 //    result is the same softmax either way.
-//  * K/V rows of keys past the request's end are zeroed (V) or masked (K), so
-//    page-tail garbage cannot reach the output through 0*NaN.
+//  * Keys past the request's end are read from the request's first visible key
+//    row instead, so page-tail garbage (possibly NaN) is never loaded; their
+//    logits are masked, so their weight is exactly zero.
 //  * Epilogue: a unit finished inside the workgroup writes bf16 output;
 //    otherwise fp32 normalised partials + log2-sum-exp for combine.hip.
 #include <type_traits>
@@ -81,6 +82,16 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const unsigned char* p)
     return __builtin_bit_cast(u32x2_t, v);
 }
 
+// Max over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950
+// row-swap instructions, which stay in the VALU instead of going through LDS.
+__device__ __forceinline__ float max_across_groups(float x)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even)
@@ -96,9 +107,21 @@ struct Cfg {
     static constexpr int DT = DW / 16;      // PV d-tiles per wave
     static constexpr int ROWS = 16 * RT;
     static constexpr int NOWN = (RT + kWaves - 1) / kWaves;  // row tiles owned per wave
-    // With head_dim 512 and 4-5 row tiles the Q^T operands live in LDS, not registers:
-    // the register file cannot hold them next to the 128-160 accumulators.
-    static constexpr bool QLDS = DP == 512 && RT >= 4;
+    // K/V loads: a key's d-slice is NCH 16-byte chunks, read by NCH consecutive lanes, so
+    // one load instruction covers KPI whole slices (256 contiguous bytes per key at
+    // head_dim 512); a 32-key tile takes NI loads each of K and V per wave.
+    static constexpr int NCH = DW / 8;
+    static constexpr int KPI = 64 / NCH;
+    static constexpr int NI = kTK / KPI;
+    static constexpr int KSH = NCH == 16 ? 0 : NCH == 8 ? 1 : 2;
+    // K tile, row-major [key][d_local] in 16-byte chunks; chunk c of row r sits at
+    // c ^ ((r >> KSH) % NCH), which keeps both the row-wise stores and the MFMA-order
+    // reads (16 keys at one chunk) free of bank conflicts.
+    static constexpr int KROW = DW * 2;
+    static __device__ __forceinline__ int kofs(int row, int chunk)
+    {
+        return row * KROW + 16 * (chunk ^ ((row >> KSH) & (NCH - 1)));
+    }
     // V tile, row-major [key][d_local], addressed in 8-byte chunks.  A transposing
     // read touches four key rows of 32 bytes per 16-lane group (eight rows per
     // 32-lane pass).  Rows of 256 bytes XOR the chunk index with 4*(row % 8), which
@@ -114,17 +137,19 @@ struct Cfg {
     static constexpr int PX_BYTES = RT * 64 * 16;               // P^T (B operand) [b][lane]
     static constexpr int V_BYTES_PER_WAVE = kTK * VROW;
     static constexpr int V_BYTES = kWaves * V_BYTES_PER_WAVE;
+    static constexpr int K_BYTES_PER_WAVE = kTK * KROW;
+    static constexpr int K_BYTES = kWaves * K_BYTES_PER_WAVE;
     static constexpr int ROWF_BYTES = ROWS * 4;
     static constexpr int OFF_SX = 0;
     static constexpr int OFF_PX = OFF_SX + SX_BYTES;
     static constexpr int OFF_V = OFF_PX + PX_BYTES;
-    static constexpr int OFF_LSUM = OFF_V + V_BYTES;
+    static constexpr int OFF_K = OFF_V + V_BYTES;
+    static constexpr int OFF_LSUM = OFF_K + K_BYTES;
     static constexpr int OFF_MREF = OFF_LSUM + ROWF_BYTES;
     static constexpr int OFF_FLAG = OFF_MREF + ROWF_BYTES;
-    static constexpr int OFF_Q = OFF_FLAG + 16 * 4;
-    static constexpr int Q_BYTES = QLDS ? RT * KS * kThreads * 16 : 0;
-    static constexpr int LDS_BYTES = OFF_Q + Q_BYTES;
+    static constexpr int LDS_BYTES = OFF_FLAG + 16 * 4;
     static_assert(KS >= 1 && DT >= 1, "head_dim too small for the d-split");
+    static_assert(NCH >= 4 && NCH <= 16 && KPI * NCH == 64 && NI * KPI == kTK, "load geometry");
     static_assert(RT <= 16, "flag array");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -145,7 +170,6 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
     float* lsum_s = reinterpret_cast<float*>(lds + C::OFF_LSUM);
     float* mref_s = reinterpret_cast<float*>(lds + C::OFF_MREF);
     int* flag_s = reinterpret_cast<int*>(lds + C::OFF_FLAG);
-    u32x4_t* qls = reinterpret_cast<u32x4_t*>(lds + C::OFF_Q);  // [b][s][thread] when QLDS
 
     const Decomp& d = a.d;
     const int wave = threadIdx.x >> 6;
@@ -154,6 +178,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
     const int grp4 = lane >> 4;
     const int wbase = wave * DW;  // first d of this wave's slice
     unsigned char* vls = lds + C::OFF_V + wave * C::V_BYTES_PER_WAVE;
+    unsigned char* kls = lds + C::OFF_K + wave * C::K_BYTES_PER_WAVE;
+    constexpr int NI = C::NI;
+    constexpr int KPI = C::KPI;
+    const int kl = lane / C::NCH;  // key of this lane within a load's KPI keys
+    const int sl = lane % C::NCH;  // 16-byte chunk of this lane within the key's d-slice
+    // this lane's chunk exists (always, unless head_dim < padded head_dim); an absent one
+    // reads the row start, finite data that meets a zero Q chunk or an unstored column
+    const bool lval = EXACT || wbase + 8 * sl < a.D;
 
     const int32_t wg = logical_wg(blockIdx.x, d.P);
     const int32_t D = a.D;
@@ -212,9 +244,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
             }
             const int64_t off = pos - rbase;
             const int32_t unit = (int32_t)(off / g.ntiles);
-            const int32_t t0 = (int32_t)(off % g.ntiles);
+            // segment bounds are wave-uniform; readfirstlane lets the compiler keep the tile
+            // loop in scalar control flow with exact memory-counter waits
+            const int32_t t0 = __builtin_amdgcn_readfirstlane((int32_t)(off % g.ntiles));
             const int64_t seg_end = min(end, rbase + (int64_t)(unit + 1) * g.ntiles);
-            const int32_t t1 = (int32_t)(seg_end - rbase - (int64_t)unit * g.ntiles);
+            const int32_t t1 = __builtin_amdgcn_readfirstlane((int32_t)(seg_end - rbase - (int64_t)unit * g.ntiles));
             const int this_seg = seg++;
             pos = seg_end;
             if constexpr (PHASE == 1) {
@@ -236,9 +270,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
             const int64_t head_off = (int64_t)kvh * D;
 
             // ---------------- Q^T (B operand) for the unit ----------------
-            bf16x8_t qf[C::QLDS ? 1 : RT][KS];
-            if constexpr (C::QLDS)
-                __syncthreads();  // the previous segment may still read Q from LDS
+            bf16x8_t qf[RT][KS];
 #pragma unroll
             for (int b = 0; b < RT; ++b) {
                 const int32_t row = b * 16 + l16;
@@ -255,39 +287,62 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                     x[1] = keep ? x[1] : 0u;
                     x[2] = keep ? x[2] : 0u;
                     x[3] = keep ? x[3] : 0u;
-                    if constexpr (C::QLDS)
-                        qls[(b * KS + s) * kThreads + threadIdx.x] = x;
-                    else
-                        qf[b][s] = as_bf16x8(x);
+                    qf[b][s] = as_bf16x8(x);
                 }
             }
 
-            // Row offset (elements) of this lane's key in half h of tile t, and whether it
-            // exists.  Keys past the end use the request's first key row so that every load
-            // stays in bounds; their V is zeroed and their logits are masked.
+            // Element offset of the request's first visible key row: keys past the end (and
+            // tiles past the segment) read it, so every load stays in bounds and finite.
             const int64_t safe_row =
                 ((int64_t)pt[g.kv_lo >> a.page_shift] * psize + (g.kv_lo & (psize - 1))) * d.Hkv * (int64_t)D;
-            // A tile key is located in two steps so that no wait lands on loads in flight:
-            // key_page() reads the page-table entry (at a clamped, always valid index) one
-            // tile ahead; key_row() turns it into a row offset only when the tile's K/V
-            // are requested.  Keys past the end use the request's first key row so that
-            // every load stays in bounds; their V is zeroed and their logits are masked.
-            auto key_page = [&](int32_t t, int h) -> int32_t {
-                const int32_t key = g.kv_lo + t * kTK + 16 * h + l16;
-                const int32_t kc = key < T ? key : T - 1;
-                return pt[kc >> a.page_shift];
+            // Tile keys are located in two steps so that no wait lands on loads in flight:
+            // tile_page() reads, one tile ahead, the page-table entry of key lane % 32 of the
+            // tile (at a clamped, always valid index); tile_rows() hands each lane the
+            // entries of its NI keys when the tile's K/V are requested -- two lane reads when
+            // a page spans 16 keys, else a shuffle per key.  Keys past the end and tiles
+            // past the segment get the safe row.
+            auto tile_page = [&](int32_t t) -> int32_t {
+                const int32_t key = g.kv_lo + t * kTK + (lane & 31);
+                return pt[(key < T ? key : T - 1) >> a.page_shift];
             };
-            auto key_row = [&](int32_t t, int h, int32_t page, bool& valid) -> int64_t {
-                const int32_t key = g.kv_lo + t * kTK + 16 * h + l16;
-                valid = key < T;
-                const int64_t row = ((int64_t)page * psize + (key & (psize - 1))) * d.Hkv * (int64_t)D;
-                return valid ? row : safe_row;
+            const int32_t hkvd = d.Hkv * D;  // elements per key row
+            auto tile_rows = [&](int32_t t, int32_t pgl, int64_t (&rows)[NI]) {
+                const int32_t k0 = g.kv_lo + t * kTK;
+                // keys at or past kend read the safe row (kend = 0 for a tile past the segment)
+                const int32_t kend = t < t1 ? T : 0;
+                int32_t page[NI];
+                if (a.page_shift >= 4) {
+                    const int32_t p0 = __builtin_amdgcn_readlane(pgl, 0);
+                    const int32_t p1 = __builtin_amdgcn_readlane(pgl, 16);
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+                        page[i] = (i * KPI) & 16 ? p1 : p0;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+                        page[i] = __builtin_amdgcn_ds_bpermute(4 * (i * KPI + kl), pgl);
+                }
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int32_t key = k0 + i * KPI + kl;
+                    const uint64_t slot = (uint64_t)(uint32_t)page[i] * (uint32_t)psize + (uint32_t)(key & (psize - 1));
+                    const int64_t row = (int64_t)(slot * (uint32_t)hkvd);
+                    rows[i] = key < kend ? row : safe_row;
+                }
             };
 
             float m_fix[NOWN];
+            // visible key range [rlo, rhi] of this lane's query row in each owned row tile
+            int32_t rlo[NOWN], rhi[NOWN];
 #pragma unroll
-            for (int ob = 0; ob < NOWN; ++ob)
+            for (int ob = 0; ob < NOWN; ++ob) {
                 m_fix[ob] = -INFINITY;
+                const int32_t row = (ob * kWaves + wave) * 16 + l16;
+                const bool rv = row < rows_here;
+                query_range(L, n, (row0 + (rv ? row : 0)) / G, is_causal, d.window, rlo[ob], rhi[ob]);
+                if (!rv)
+                    rhi[ob] = -1;  // padding row: nothing visible
+            }
 
             // One pass over the segment's tiles (MODE kLazy, kMaxScan or kFixed).  Returns
             // true when a kLazy pass met a tile beyond its reference bound.
@@ -307,97 +362,81 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                 }
                 bool aborted = false;
 
-                int64_t krow[2];
-                int32_t kpage_next[2];
-                bool kval[2];
-                u32x4_t kr[2][KS], vr[2][KS];
-                auto issue_kv = [&]() {
+                int64_t rows[NI];
+                int32_t pg_next;
+                u32x4_t kr[NI], vr[NI];
+                const int64_t lane_off = head_off + (lval ? wbase + 8 * sl : 0);
+                auto issue = [&](const uint16_t* base, u32x4_t (&dst)[NI]) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint16_t* kp = a.k_pages + krow[h] + head_off;
-                        const uint16_t* vp = a.v_pages + krow[h] + head_off;
-#pragma unroll
-                        for (int s = 0; s < KS; ++s) {
-                            const int e = (EXACT || dval[s]) ? wbase + 32 * s + 8 * grp4 : 0;
-                            kr[h][s] = ldg16_stream(kp + e);
-                            if constexpr (MODE != kMaxScan)
-                                vr[h][s] = ldg16_stream(vp + e);
-                        }
-                    }
+                    for (int i = 0; i < NI; ++i)
+                        dst[i] = ldg16_stream(base + rows[i] + lane_off);
                 };
 
-                // One 32-key tile per step: the registers of tile t are consumed first (V
-                // into LDS, K into the S^T MFMAs); then tile t+1 is requested into the same
-                // registers, so its loads overlap the softmax and PV product of tile t.
-                krow[0] = key_row(t0, 0, key_page(t0, 0), kval[0]);
-                krow[1] = key_row(t0, 1, key_page(t0, 1), kval[1]);
-                if (t0 + 1 < t1) {
-                    kpage_next[0] = key_page(t0 + 1, 0);
-                    kpage_next[1] = key_page(t0 + 1, 1);
-                }
-                issue_kv();
+                // One 32-key tile per step.  At the top of step t the registers holding the
+                // K/V of tile t are written to LDS and at once refilled with tile t+1, which
+                // so has a whole step to arrive.  Every request is unconditional (a tile
+                // past the segment reads the safe row, page entries are read at clamped
+                // indices): the loop has no divergent branches and each wait on the memory
+                // counter is exact.  The issue order (page entries, V, K) is pinned with
+                // scheduling barriers, here and in the loop: the compiler's waits at the
+                // loop head are exact only if both paths into it issue in the same order.
+                tile_rows(t0, tile_page(t0), rows);
+                pg_next = tile_page(t0 + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                issue(a.k_pages, kr);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (MODE != kMaxScan)
+                    issue(a.v_pages, vr);
+                __builtin_amdgcn_sched_barrier(0);
                 // An abandoned lazy segment leaves by the loop condition only: an exit between
                 // the softmax and the PV product would make the compiler keep a second copy of
                 // every accumulator.  The tile that triggered it still runs its (discarded) PV.
                 for (int32_t t = t0; t < t1 && !aborted; ++t) {
                     const int32_t k0 = g.kv_lo + t * kTK;
-                    // (1) this wave's V slice -> LDS [key][d_local]; absent keys/d are zero
+                    // (1) this wave's K and V slices -> LDS [key][d_local].  Keys past the
+                    // request hold the safe row and d past head_dim the row start: finite
+                    // values whose weight (masked logit) or output column (never stored) is 0.
                     if constexpr (MODE != kMaxScan) {
 #pragma unroll
-                        for (int h = 0; h < 2; ++h)
-#pragma unroll
-                            for (int s = 0; s < KS; ++s) {
-                                const bool keep = kval[h] && dval[s];
-                                u32x4_t x = vr[h][s];
-                                x[0] = keep ? x[0] : 0u;
-                                x[1] = keep ? x[1] : 0u;
-                                x[2] = keep ? x[2] : 0u;
-                                x[3] = keep ? x[3] : 0u;
-                                *reinterpret_cast<u32x4_t*>(vls + C::vofs(16 * h + l16, 8 * s + 2 * grp4)) = x;
-                            }
+                        for (int i = 0; i < NI; ++i)
+                            *reinterpret_cast<u32x4_t*>(vls + C::vofs(i * KPI + kl, 2 * sl)) = vr[i];
                     }
-                    // (2) partial S^T over this wave's d-slice (absent d: Q is zero there;
-                    //     absent keys are masked below, whatever their K holds)
+#pragma unroll
+                    for (int i = 0; i < NI; ++i)
+                        *reinterpret_cast<u32x4_t*>(kls + C::kofs(i * KPI + kl, sl)) = kr[i];
+                    // request tile t+1 (page entries of t+2 first, so that waiting for them
+                    // later never waits for K/V)
+                    tile_rows(t + 1, pg_next, rows);
+                    pg_next = tile_page(t + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue(a.k_pages, kr);
+                    __builtin_amdgcn_sched_barrier(0);
+                    // (2) partial S^T over this wave's d-slice (absent d: Q is zero there and K
+                    //     finite; absent keys are masked below).  A operand: key 16h + l16,
+                    //     d chunk 4s + grp4 of the slice.
                     bf16x8_t kb[2][KS];
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int s = 0; s < KS; ++s) {
-                            u32x4_t kx = kr[h][s];
-                            kx[0] = dval[s] ? kx[0] : 0u;
-                            kx[1] = dval[s] ? kx[1] : 0u;
-                            kx[2] = dval[s] ? kx[2] : 0u;
-                            kx[3] = dval[s] ? kx[3] : 0u;
-                            kb[h][s] = as_bf16x8(kx);
-                        }
+                        for (int s = 0; s < KS; ++s)
+                            kb[h][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kls + C::kofs(16 * h + l16, 4 * s + grp4)));
 #pragma unroll
                     for (int b = 0; b < RT; ++b) {
                         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int s = 0; s < KS; ++s) {
-                            bf16x8_t qb;
-                            if constexpr (C::QLDS)
-                                qb = as_bf16x8(qls[(b * KS + s) * kThreads + threadIdx.x]);
-                            else
-                                qb = qf[b][s];
-                            acc0 = mfma16(kb[0][s], qb, acc0);
-                            acc1 = mfma16(kb[1][s], qb, acc1);
+                            acc0 = mfma16(kb[0][s], qf[b][s], acc0);
+                            acc1 = mfma16(kb[1][s], qf[b][s], acc1);
                         }
                         sx[((wave * 2 + 0) * RT + b) * 64 + lane] = acc0;
                         sx[((wave * 2 + 1) * RT + b) * 64 + lane] = acc1;
                     }
-                    // request tile t+1 (registers are free now); the page entries of t+2 first,
-                    // so that waiting for them later never waits for the K/V of t+1
-                    if (t + 1 < t1) {
-                        krow[0] = key_row(t + 1, 0, kpage_next[0], kval[0]);
-                        krow[1] = key_row(t + 1, 1, kpage_next[1], kval[1]);
-                        if (t + 2 < t1) {
-                            kpage_next[0] = key_page(t + 2, 0);
-                            kpage_next[1] = key_page(t + 2, 1);
-                        }
-                        issue_kv();
-                    }
                     __syncthreads();
+                    // V of tile t+1: requested here rather than with K so that the two
+                    // halves of the workgroup's 64 KB do not queue at the address unit at once
+                    if constexpr (MODE != kMaxScan)
+                        issue(a.v_pages, vr);
+                    __builtin_amdgcn_sched_barrier(0);
                     // (3) owners: reduce, mask, softmax, publish P^T
 #pragma unroll
                     for (int ob = 0; ob < NOWN; ++ob) {
@@ -414,13 +453,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                                 for (int e = 0; e < 4; ++e)
                                     z[h * 4 + e] = s4[e];
                             }
-                            const int32_t row = b * 16 + l16;
-                            const bool rv = row < rows_here;
-                            const int32_t qi = (row0 + (rv ? row : 0)) / G;
-                            int32_t lo, hi;
-                            query_range(L, n, qi, is_causal, d.window, lo, hi);
-                            if (!rv)
-                                hi = -1;  // padding row: nothing visible
+                            const int32_t lo = rlo[ob], hi = rhi[ob];
                             float tmax = -INFINITY;
 #pragma unroll
                             for (int h = 0; h < 2; ++h)
@@ -432,8 +465,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                                     z[h * 4 + e] = zz;
                                     tmax = fmaxf(tmax, zz);
                                 }
-                            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-                            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+                            tmax = max_across_groups(tmax);
                             if constexpr (MODE == kMaxScan) {
                                 m_fix[ob] = fmaxf(m_fix[ob], tmax);
                             } else {
@@ -450,8 +482,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                                 float psum = 0.f;
 #pragma unroll
                                 for (int e2 = 0; e2 < 4; ++e2) {
-                                    const uint32_t w2 =
-                                        pack_bf16x2(exp2f(z[2 * e2] - mu), exp2f(z[2 * e2 + 1] - mu));
+                                    const uint32_t w2 = pack_bf16x2(__builtin_amdgcn_exp2f(z[2 * e2] - mu),
+                                                                    __builtin_amdgcn_exp2f(z[2 * e2 + 1] - mu));
                                     pk[e2] = w2;
                                     // the denominator sums the same bf16-rounded weights PV uses
                                     psum += __uint_as_float(w2 << 16) + __uint_as_float(w2 & 0xffff0000u);
@@ -475,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
                         for (int b = 0; b < RT; ++b)
                             anyover |= flag_s[b];
-                        aborted = anyover != 0;
+                        aborted = __builtin_amdgcn_readfirstlane(anyover) != 0;
                     }
                     // (4) O^T += V^T P^T for this wave's d-slice
                     // A operand V^T: lane l holds d = 16c + l%16 at key slots 4*grp4 + 0..3
