@@ -47,6 +47,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -95,7 +96,6 @@ __device__ __forceinline__ float max_across_groups(float x)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even)
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
 }
@@ -332,16 +332,27 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
             };
 
             float m_fix[NOWN];
-            // visible key range [rlo, rhi] of this lane's query row in each owned row tile
-            int32_t rlo[NOWN], rhi[NOWN];
+            // Visible key range [rlo, rhi] of this lane's query row in each owned row tile, and
+            // the keys [ilo, ihi] every real row of the tile sees: a tile inside that range
+            // needs no mask (padding rows then get finite weights that reach no output).
+            int32_t rlo[NOWN], rhi[NOWN], ilo[NOWN], ihi[NOWN];
 #pragma unroll
             for (int ob = 0; ob < NOWN; ++ob) {
                 m_fix[ob] = -INFINITY;
                 const int32_t row = (ob * kWaves + wave) * 16 + l16;
                 const bool rv = row < rows_here;
                 query_range(L, n, (row0 + (rv ? row : 0)) / G, is_causal, d.window, rlo[ob], rhi[ob]);
+                int32_t lo_all = rv ? rlo[ob] : INT32_MIN;
+                int32_t hi_all = rv ? rhi[ob] : INT32_MAX;
                 if (!rv)
                     rhi[ob] = -1;  // padding row: nothing visible
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    lo_all = max(lo_all, __shfl_xor(lo_all, off));
+                    hi_all = min(hi_all, __shfl_xor(hi_all, off));
+                }
+                ilo[ob] = __builtin_amdgcn_readfirstlane(lo_all);
+                ihi[ob] = __builtin_amdgcn_readfirstlane(hi_all);
             }
 
             // One pass over the segment's tiles (MODE kLazy, kMaxScan or kFixed).  Returns
@@ -442,29 +453,42 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                     for (int ob = 0; ob < NOWN; ++ob) {
                         const int b = ob * kWaves + wave;
                         if (b < RT) {
+                            // all eight partials are requested before any is summed, so that the
+                            // LDS latency is paid once rather than once per partial
+                            f32x4_t part[2][kWaves];
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                for (int ww = 0; ww < kWaves; ++ww)
+                                    part[h][ww] = sx[((ww * 2 + h) * RT + b) * 64 + lane];
                             float z[8];
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
-                                f32x4_t s4 = sx[((0 * 2 + h) * RT + b) * 64 + lane];
-#pragma unroll
-                                for (int ww = 1; ww < kWaves; ++ww)
-                                    s4 += sx[((ww * 2 + h) * RT + b) * 64 + lane];
+                                const f32x4_t s4 = (part[h][0] + part[h][1]) + (part[h][2] + part[h][3]);
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
                                     z[h * 4 + e] = s4[e];
                             }
-                            const int32_t lo = rlo[ob], hi = rhi[ob];
                             float tmax = -INFINITY;
+                            if (k0 >= ilo[ob] && k0 + kTK - 1 <= ihi[ob]) {
 #pragma unroll
-                            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const int32_t key = k0 + 16 * h + 4 * grp4 + e;
-                                    const bool vis = key >= lo && key <= hi;
-                                    const float zz = vis ? z[h * 4 + e] * a.scale_log2 : -INFINITY;
-                                    z[h * 4 + e] = zz;
-                                    tmax = fmaxf(tmax, zz);
+                                for (int e = 0; e < 8; ++e) {
+                                    z[e] *= a.scale_log2;
+                                    tmax = fmaxf(tmax, z[e]);
                                 }
+                            } else {
+                                const int32_t lo = rlo[ob], hi = rhi[ob];
+#pragma unroll
+                                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) {
+                                        const int32_t key = k0 + 16 * h + 4 * grp4 + e;
+                                        const bool vis = key >= lo && key <= hi;
+                                        const float zz = vis ? z[h * 4 + e] * a.scale_log2 : -INFINITY;
+                                        z[h * 4 + e] = zz;
+                                        tmax = fmaxf(tmax, zz);
+                                    }
+                            }
                             tmax = max_across_groups(tmax);
                             if constexpr (MODE == kMaxScan) {
                                 m_fix[ob] = fmaxf(m_fix[ob], tmax);
@@ -479,16 +503,19 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                                 }
                                 const float mu = (m_new == -INFINITY) ? 0.f : m_new;
                                 u32x4_t pk;
-                                float psum = 0.f;
+                                // the denominator sums the same bf16-rounded weights PV uses
+                                // (a dot product of each packed pair with (1, 1))
+                                const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+                                float psum = l_run[ob];
 #pragma unroll
                                 for (int e2 = 0; e2 < 4; ++e2) {
                                     const uint32_t w2 = pack_bf16x2(__builtin_amdgcn_exp2f(z[2 * e2] - mu),
                                                                     __builtin_amdgcn_exp2f(z[2 * e2 + 1] - mu));
                                     pk[e2] = w2;
-                                    // the denominator sums the same bf16-rounded weights PV uses
-                                    psum += __uint_as_float(w2 << 16) + __uint_as_float(w2 & 0xffff0000u);
+                                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2), ones, psum,
+                                                                          false);
                                 }
-                                l_run[ob] += psum;
+                                l_run[ob] = psum;
                                 m_run[ob] = m_new;
                                 px[b * 64 + lane] = pk;
                                 if constexpr (MODE == kLazy) {
