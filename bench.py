@@ -4,14 +4,21 @@
 
 A step is one whole dflash_block_attn call (attention kernel + split-KV
 combine) over one batch of the named synthetic workload, inputs resident in
-HBM.  Between steps a 1 GiB buffer is read (outside the timed events) so that
-the 256 MB Infinity Cache does not hold K/V from the previous step.  The flush
-only reads: a flush that writes leaves up to 256 MB of dirty lines whose
-write-back would then be charged to the timed kernel.
+HBM.  Between steps a 1 GiB buffer is read by the library's streaming-read
+kernel (outside the timed events) so that the 256 MB Infinity Cache does not
+hold K/V from the previous step.  The flush only reads: a flush that writes
+leaves up to 256 MB of dirty lines whose write-back would then be charged to
+the timed kernel.  The same streaming read, timed, is the measured achievable
+read bandwidth the K/V rate is also compared with.
 
 Printed (one JSON line): query-tokens/s over the timed steps, the achieved
-K/V HBM bandwidth of the attention kernel against the 8 TB/s peak, and the
-fp64 CPU oracle timed on a bounded sample of the same workload.
+K/V HBM bandwidth of the attention kernel against the 8 TB/s peak and against
+the measured streaming read, and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
+
+    python bench.py --summarize-pmc FETCH_CSV WRITE_CSV
+turns two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE)
+into the HBM-traffic record the "traffic" field reads.
 """
 from __future__ import annotations
 
@@ -29,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "query-tokens/s + K/V HBM GB/s (% of peak) for block attention, 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_mfma_c3_global_d512.json")
+FLUSH_BYTES = 1 << 30
 KERNEL_SOURCES = ["attn_mfma.hip", "device_common.h", "decomp.h"]
 
 
@@ -92,6 +100,58 @@ def traffic_for(kernel_hash: str, launches_bytes: float):
     return rec.get("bytes_per_launch")
 
 
+def _pmc_means(path: str, counter: str) -> dict:
+    """Mean counter value per dispatch, per kernel name, from a rocprofv3 counter CSV."""
+    import csv
+
+    acc = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, config: str) -> dict:
+    """HBM bytes per launch of the attention kernel from FETCH_SIZE / WRITE_SIZE runs.
+
+    Each counter (KiB per dispatch) is scaled by what it reads for a kernel of
+    known size in the same run: the 1 GiB streaming-read flush for FETCH_SIZE,
+    the 1 GiB fill that initialises the flush buffer for WRITE_SIZE."""
+    import workloads
+
+    fetch = _pmc_means(fetch_csv, "FETCH_SIZE")
+    write = _pmc_means(write_csv, "WRITE_SIZE")
+
+    def pick(table, key):
+        names = [k for k in table if key in k]
+        if len(names) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {names}")
+        return names[0], table[names[0]]
+
+    attn_name, attn_fetch = pick(fetch, "attn_mfma_kernel")
+    _, attn_write = pick(write, "attn_mfma_kernel")
+    _, read_cal = pick(fetch, "stream_read_kernel")
+    _, write_cal = pick(write, "FillFunctor")
+    f_read = FLUSH_BYTES / (read_cal * 1024.0)
+    f_write = FLUSH_BYTES / (write_cal * 1024.0)
+    fetch_b = attn_fetch * 1024.0 * f_read
+    write_b = attn_write * 1024.0 * f_write
+    kv = visible_kv_bytes(workloads.make(config, poison=False))
+    return {
+        "kernel": attn_name, "workload": config, "kernel_sha": kernel_source_hash(),
+        "fetch_kib_per_launch": attn_fetch, "write_kib_per_launch": attn_write,
+        "read_calibration": {"kernel": "dflash stream_read", "known_bytes": FLUSH_BYTES, "fetch_kib": read_cal,
+                             "factor": f_read},
+        "write_calibration": {"kernel": "torch fill_ (flush buffer init)", "known_bytes": FLUSH_BYTES,
+                              "write_kib": write_cal, "factor": f_write},
+        "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+        "bytes_per_launch": fetch_b + write_b, "algorithmic_kv_bytes": kv,
+        "over_fetch_ratio": fetch_b / kv,
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,7 +162,18 @@ def main(argv=None) -> int:
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        rec = summarize_pmc(*args.summarize_pmc, args.config)
+        rec["command"] = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --kernel-include-regex "
+                          "'attn_mfma|stream_read|FillFunctor' -f csv -d <dir> -o run -- "
+                          f"python3 bench.py --config {args.config} --steps 5 --warmup 2 --no-cpu-baseline")
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec, indent=1))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -141,8 +212,15 @@ def main(argv=None) -> int:
     plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
-    flush = None if args.no_flush else torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush.fill_(1.0)  # also the known-size write the WRITE_SIZE counter is calibrated with
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)  # receives the XOR of each pass
     stream = torch.cuda.current_stream(dev)
+
+    def stream_read():
+        st = nb.dflash_stream_read(flush, FLUSH_BYTES, sink, stream.cuda_stream)
+        if st != nb.DFLASH_OK:
+            raise nb.DFlashError(st, nb.dflash_last_error_message())
 
     n_ev = args.warmup + args.steps
     call0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -154,8 +232,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     def step(i):
-        if flush is not None:
-            flush.sum()  # reads 1 GiB; the scalar result is discarded
+        if not args.no_flush:
+            stream_read()
         desc.event_attn_begin, desc.event_attn_end = att0[i].cuda_event, att1[i].cuda_event
         call0[i].record(stream)
         st = nb.dflash_block_attn(q, kp, vp, pt, ctx, blk, wl.Hq, wl.Hkv, wl.D, causal, wl.window, wl.scale, out,
@@ -175,6 +253,16 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
 
+    # measured achievable read bandwidth: the same streaming read, timed on its own
+    sr0 = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    sr1 = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for i in range(6):
+        sr0[i].record(stream)
+        stream_read()
+        sr1[i].record(stream)
+    torch.cuda.synchronize()
+    stream_gbps = FLUSH_BYTES / (np.mean([sr0[i].elapsed_time(sr1[i]) for i in range(1, 6)]) / 1e3) / 1e9
+
     call_ms = np.array([call0[i].elapsed_time(call1[i]) for i in range(args.warmup, n_ev)])
     att_ms = np.array([att0[i].elapsed_time(att1[i]) for i in range(args.warmup, n_ev)])
     tokens = wl.total_q
@@ -186,7 +274,7 @@ def main(argv=None) -> int:
     print(f"[bench] call mean {call_ms.mean()*1e3:.1f} us (p10 {np.percentile(call_ms,10)*1e3:.1f}, "
           f"p90 {np.percentile(call_ms,90)*1e3:.1f}); attention kernel mean {att_ms.mean()*1e3:.1f} us; "
           f"K/V {kv_bytes/1e6:.1f} MB -> {achieved:.0f} GB/s kernel, {call_gbps:.0f} GB/s call; "
-          f"wall {t_wall:.3f} s", file=sys.stderr, flush=True)
+          f"wall {t_wall:.3f} s; streaming read {stream_gbps:.0f} GB/s", file=sys.stderr, flush=True)
 
     khash = kernel_source_hash()
     traffic = traffic_for(khash, kv_bytes)
@@ -217,6 +305,8 @@ def main(argv=None) -> int:
         },
         "kv_hbm_gbps": call_gbps,
         "kv_hbm_frac_of_peak": call_gbps / HBM_PEAK_GBPS,
+        "stream_read_gbps": stream_gbps,
+        "attn_kv_frac_of_stream_read": achieved / stream_gbps,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,

@@ -147,6 +147,22 @@ const char* dflash_last_error_message(void);
 /* DFLASH_ABI_VERSION of the built library. */
 int dflash_abi_version(void);
 
+/*
+ * Measurement helper, not part of the attention: reads `bytes` of device memory
+ * at `buf` once, with the same streaming (nontemporal) 16-byte loads the
+ * attention kernel uses for K/V, and XORs every 32-bit word it read into
+ * sink[0] (one atomic per wavefront; clear sink[0] first to get the XOR of the
+ * buffer).  Timing it gives the achievable HBM read bandwidth that K/V GB/s is
+ * reported against, next to the 8 TB/s specification; a pass over a buffer
+ * larger than the last-level cache is also a flush that leaves no dirty lines.
+ *   buf    device pointer, 16-byte aligned; bytes a multiple of 16 (0 is a no-op)
+ *   sink   device uint32_t[1], caller-owned
+ *   stream hipStream_t (NULL = default stream); asynchronous, stream-ordered
+ * Returns DFLASH_ERR_INVALID_ARGUMENT for a NULL/misaligned pointer or size,
+ * DFLASH_ERR_HIP if the launch fails.
+ */
+int dflash_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,11 @@ def dflash_abi_version() -> int:
     return _lib.load().dflash_abi_version()
 
 
+def dflash_stream_read(buf, nbytes: int, sink, stream) -> int:
+    """Measurement helper: one streaming read of nbytes at buf (see the C header)."""
+    return _lib.load().dflash_stream_read(_ptr(buf), nbytes, _ptr(sink), stream)
+
+
 def dflash_status_string(status: int) -> str:
     return _lib.load().dflash_status_string(status).decode()
 

@@ -85,5 +85,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_last_error_message.restype = ctypes.c_char_p
     lib.dflash_abi_version.argtypes = []
     lib.dflash_abi_version.restype = ctypes.c_int
+    lib.dflash_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.dflash_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib

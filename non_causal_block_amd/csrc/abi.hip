@@ -192,6 +192,27 @@ extern "C" {
 
 int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
 
+int dflash_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream)
+{
+    if (bytes == 0)
+        return DFLASH_OK;
+    if (!buf || !sink)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "stream_read: buf and sink must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(buf) & 15) || (bytes & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "stream_read: buf and bytes must be 16-byte multiples, sink 4-byte aligned");
+    int cus = 0;
+    const int st = device_cus(&cus);
+    if (st != DFLASH_OK)
+        return st;
+    // four workgroups per compute unit keep enough 16-byte loads in flight
+    const int64_t need = (int64_t)((bytes / 16 + 255) / 256);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(need, (int64_t)cus * 4));
+    const hipError_t e = dflash::launch_stream_read(buf, bytes, sink, grid, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "stream_read launch failed: %s", hipGetErrorString(e));
+    return DFLASH_OK;
+}
+
 const char* dflash_status_string(int status)
 {
     switch (status) {

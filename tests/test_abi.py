@@ -32,9 +32,17 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_stream_read_rejects_bad_arguments(lib):
+    # validation happens on the host, before any HIP call
+    assert nb.dflash_stream_read(None, 16, None, None) == nb.DFLASH_ERR_INVALID_ARGUMENT
+    assert nb.dflash_stream_read(0x1000, 15, 0x2000, None) == nb.DFLASH_ERR_INVALID_ARGUMENT
+    assert nb.dflash_stream_read(0x1008, 16, 0x2000, None) == nb.DFLASH_ERR_INVALID_ARGUMENT
+    assert nb.dflash_stream_read(0x1000, 0, 0x2000, None) == nb.DFLASH_OK  # nothing to read
 
 
 def test_abi_version(lib):
