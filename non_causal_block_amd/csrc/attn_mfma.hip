@@ -49,8 +49,14 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+// Waves per workgroup: the head dimension is split over them (DP / WAVES d each).
+// Four, one per SIMD.  An 8-way split at head_dim 512 (two waves per SIMD, 80
+// accumulators each) passes the same tests but ran about 5% slower on C3: the
+// barriers keep both waves of a SIMD in the same phase, and each row-tile owner
+// then sums twice as many partial products.
+constexpr int waves_for(int /*dp*/) { return 4; }
+template <int DP>
+constexpr int threads_for = waves_for(DP) * 64;
 constexpr int kTK = 32;              // keys per tile (two 16-key MFMA tiles)
 constexpr float kLazyBound = 32.0f;  // log2 units a row max may exceed its reference by
 constexpr int kLazy = 0, kMaxScan = 1, kFixed = 2;
@@ -102,11 +108,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 template <int DP, int RT>
 struct Cfg {
-    static constexpr int DW = DP / kWaves;  // d per wave
+    static constexpr int WAVES = waves_for(DP);
+    static constexpr int THREADS = WAVES * 64;
+    static constexpr int DW = DP / WAVES;  // d per wave
     static constexpr int KS = DW / 32;      // QK^T k-steps per wave
     static constexpr int DT = DW / 16;      // PV d-tiles per wave
     static constexpr int ROWS = 16 * RT;
-    static constexpr int NOWN = (RT + kWaves - 1) / kWaves;  // row tiles owned per wave
+    static constexpr int NOWN = (RT + WAVES - 1) / WAVES;  // row tiles owned per wave
     // K/V loads: a key's d-slice is NCH 16-byte chunks, read by NCH consecutive lanes, so
     // one load instruction covers KPI whole slices (256 contiguous bytes per key at
     // head_dim 512); a 32-key tile takes NI loads each of K and V per wave.
@@ -133,12 +141,12 @@ struct Cfg {
         return row * VROW + 8 * (VSWZ ? chunk ^ ((row & 7) << 2) : chunk);
     }
     // LDS layout (bytes)
-    static constexpr int SX_BYTES = kWaves * 2 * RT * 64 * 16;  // partial S^T [wave][h][b][lane]
+    static constexpr int SX_BYTES = WAVES * 2 * RT * 64 * 16;  // partial S^T [wave][h][b][lane]
     static constexpr int PX_BYTES = RT * 64 * 16;               // P^T (B operand) [b][lane]
     static constexpr int V_BYTES_PER_WAVE = kTK * VROW;
-    static constexpr int V_BYTES = kWaves * V_BYTES_PER_WAVE;
+    static constexpr int V_BYTES = WAVES * V_BYTES_PER_WAVE;
     static constexpr int K_BYTES_PER_WAVE = kTK * KROW;
-    static constexpr int K_BYTES = kWaves * K_BYTES_PER_WAVE;
+    static constexpr int K_BYTES = WAVES * K_BYTES_PER_WAVE;
     static constexpr int ROWF_BYTES = ROWS * 4;
     static constexpr int OFF_SX = 0;
     static constexpr int OFF_PX = OFF_SX + SX_BYTES;
@@ -156,9 +164,10 @@ struct Cfg {
 
 // EXACT: head_dim == DP, so every d-chunk exists and no lane needs masking.
 template <int DP, int RT, bool EXACT>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
+__global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 {
     using C = Cfg<DP, RT>;
+    constexpr int WAVES = C::WAVES;
     constexpr int KS = C::KS;
     constexpr int DT = C::DT;
     constexpr int DW = C::DW;
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
 #pragma unroll
             for (int ob = 0; ob < NOWN; ++ob) {
                 m_fix[ob] = -INFINITY;
-                const int32_t row = (ob * kWaves + wave) * 16 + l16;
+                const int32_t row = (ob * WAVES + wave) * 16 + l16;
                 const bool rv = row < rows_here;
                 query_range(L, n, (row0 + (rv ? row : 0)) / G, is_causal, d.window, rlo[ob], rhi[ob]);
                 int32_t lo_all = rv ? rlo[ob] : INT32_MIN;
@@ -451,23 +460,25 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
                     // (3) owners: reduce, mask, softmax, publish P^T
 #pragma unroll
                     for (int ob = 0; ob < NOWN; ++ob) {
-                        const int b = ob * kWaves + wave;
+                        const int b = ob * WAVES + wave;
                         if (b < RT) {
-                            // all eight partials are requested before any is summed, so that the
-                            // LDS latency is paid once rather than once per partial
-                            f32x4_t part[2][kWaves];
-#pragma unroll
-                            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                                for (int ww = 0; ww < kWaves; ++ww)
-                                    part[h][ww] = sx[((ww * 2 + h) * RT + b) * 64 + lane];
+                            // partials are requested four at a time before any is summed, so that
+                            // the LDS latency is paid once per four
                             float z[8];
 #pragma unroll
                             for (int h = 0; h < 2; ++h) {
-                                const f32x4_t s4 = (part[h][0] + part[h][1]) + (part[h][2] + part[h][3]);
+                                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                                for (int w0 = 0; w0 < WAVES; w0 += 4) {
+                                    f32x4_t part[4];
+#pragma unroll
+                                    for (int ww = 0; ww < 4; ++ww)
+                                        part[ww] = sx[(((w0 + ww) * 2 + h) * RT + b) * 64 + lane];
+                                    acc += (part[0] + part[1]) + (part[2] + part[3]);
+                                }
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
-                                    z[h * 4 + e] = s4[e];
+                                    z[h * 4 + e] = acc[e];
                             }
                             float tmax = -INFINITY;
                             if (k0 >= ilo[ob] && k0 + kTK - 1 <= ihi[ob]) {
@@ -582,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(AttnArgs a)
             // ---------------- epilogue ----------------
 #pragma unroll
             for (int ob = 0; ob < NOWN; ++ob) {
-                const int b = ob * kWaves + wave;
+                const int b = ob * WAVES + wave;
                 if (b < RT) {
                     float l = l_run[ob];
                     l += __shfl_xor(l, 16);
@@ -643,7 +654,7 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
         if (e != hipSuccess)
             return e;
     }
-    hipLaunchKernelGGL(kern, dim3(a.d.P), dim3(kThreads), C::LDS_BYTES, stream, a);
+    hipLaunchKernelGGL(kern, dim3(a.d.P), dim3(C::THREADS), C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
@@ -680,7 +691,7 @@ template <int DP, int RT, bool EXACT>
 static int occupancy_one()
 {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT>, kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT>, Cfg<DP, RT>::THREADS,
                                                      Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
         return 0;
     return blocks;
