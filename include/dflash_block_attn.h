@@ -121,6 +121,37 @@ int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, c
                       int32_t head_dim, const uint8_t* causal, int32_t window, float scale, void* out,
                       void* stream, const dflash_batch_desc* desc);
 
+/*
+ * Block K/V append: writes each request's block K/V into the paged cache, the
+ * step that must precede the attention (the block's queries attend to the
+ * context K/V together with the block's own K/V -- kenforever1 notes, "why
+ * non-causal attention is needed" -- and those keys live in the same cache at
+ * positions L .. L+n-1).  Row t of k_new / v_new is block token i = t - q_start[r]
+ * of request r (rows packed in request order, exactly like q); it is copied to
+ * page page_table[r][(L+i) / page_size], slot (L+i) % page_size, kv-head h.
+ *   k_new, v_new     device bf16 [desc->total_q, n_kv_heads, head_dim], 16-byte aligned
+ *   k_pages, v_pages device bf16 [num_pages, page_size, n_kv_heads, head_dim]; only
+ *                    the block slots are written
+ *   page_table, ctx_lens, block_lens, desc  as for dflash_block_attn (desc->total_q
+ *                    must equal sum(block_lens); workspace and events are not used)
+ * Host-checkable errors return before anything is enqueued.  Page-table entries
+ * that the block positions need must be valid page ids (undefined otherwise).
+ */
+int dflash_block_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                           const int32_t* page_table, const int32_t* ctx_lens, const int32_t* block_lens,
+                           int32_t n_kv_heads, int32_t head_dim, void* stream, const dflash_batch_desc* desc);
+
+/*
+ * dflash_block_kv_append followed by dflash_block_attn on the same stream: one
+ * call per draft step, graph-capturable (it allocates nothing, synchronises
+ * nothing and enqueues only kernel launches).  Both halves are validated before
+ * either is enqueued; arguments as for the two calls.
+ */
+int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                             const int32_t* page_table, const int32_t* ctx_lens, const int32_t* block_lens,
+                             int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, const uint8_t* causal,
+                             int32_t window, float scale, void* out, void* stream, const dflash_batch_desc* desc);
+
 /* Scratch bytes dflash_block_attn needs for this desc and shape (desc->workspace is ignored). */
 int dflash_block_attn_workspace_size(const dflash_batch_desc* desc, int32_t n_heads, int32_t n_kv_heads,
                                      int32_t head_dim, size_t* bytes);

@@ -87,6 +87,24 @@ def dflash_block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_h
                                          scale, _ptr(out), stream, ctypes.byref(desc))
 
 
+def dflash_block_kv_append(k_new, v_new, k_pages, v_pages, page_table, ctx_lens, block_lens, n_kv_heads: int,
+                           head_dim: int, stream: Optional[int], desc: dflash_batch_desc) -> int:
+    """Raw call: write the block K/V rows into their pages; status code out."""
+    return _lib.load().dflash_block_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                              _ptr(page_table), _ptr(ctx_lens), _ptr(block_lens), n_kv_heads,
+                                              head_dim, stream, ctypes.byref(desc))
+
+
+def dflash_block_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads: int,
+                             n_kv_heads: int, head_dim: int, causal, window: int, scale: float, out,
+                             stream: Optional[int], desc: dflash_batch_desc) -> int:
+    """Raw call: append the block K/V, then attend (one stream); status code out."""
+    return _lib.load().dflash_block_attn_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                                _ptr(page_table), _ptr(ctx_lens), _ptr(block_lens), n_heads,
+                                                n_kv_heads, head_dim, _ptr(causal), window, scale, _ptr(out), stream,
+                                                ctypes.byref(desc))
+
+
 # ---- convenience -------------------------------------------------------------
 def make_desc(*, num_reqs: int, total_q: int, max_block_len: int, total_kv_len: int, page_size: int,
               max_pages_per_req: int, num_pages: int, kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0,

@@ -85,6 +85,11 @@ def load() -> ctypes.CDLL:
     lib.dflash_last_error_message.restype = ctypes.c_char_p
     lib.dflash_abi_version.argtypes = []
     lib.dflash_abi_version.restype = ctypes.c_int
+    lib.dflash_block_kv_append.argtypes = [P, P, P, P, P, P, P, i32, i32, P, ctypes.POINTER(dflash_batch_desc)]
+    lib.dflash_block_kv_append.restype = ctypes.c_int
+    lib.dflash_block_attn_append.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, P, i32, ctypes.c_float, P, P,
+                                             ctypes.POINTER(dflash_batch_desc)]
+    lib.dflash_block_attn_append.restype = ctypes.c_int
     lib.dflash_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.dflash_stream_read.restype = ctypes.c_int
     _lib = lib

@@ -186,6 +186,144 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
     return DFLASH_OK;
 }
 
+// A validated attention call: the plan and the kernel arguments.
+struct AttnCall {
+    Plan plan;
+    dflash::AttnArgs args;
+};
+
+int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                 const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
+                 int32_t head_dim, const uint8_t* causal, int32_t window, float scale, void* out,
+                 const dflash_batch_desc* desc, AttnCall* call)
+{
+    Plan& p = call->plan;
+    int st = make_plan(desc, n_heads, n_kv_heads, head_dim, &p);
+    if (st != DFLASH_OK)
+        return st;
+    if (!std::isfinite(scale))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (p.empty)
+        return DFLASH_OK;
+    if (!q || !k_pages || !v_pages || !page_table || !ctx_lens || !block_lens || !out)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "NULL device pointer (q %p, k_pages %p, v_pages %p, page_table %p, "
+                    "ctx_lens %p, block_lens %p, out %p)", q, k_pages, v_pages, page_table, ctx_lens, block_lens, out);
+    auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
+    if (mis16(q) || mis16(k_pages) || mis16(v_pages) || mis16(out))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(block_lens) & 3u))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "page_table, ctx_lens and block_lens must be 4-byte aligned");
+    if (p.ws_bytes > 0) {
+        if (!desc->workspace || desc->workspace_bytes < p.ws_bytes)
+            return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes at %p; this call needs %zu bytes",
+                        desc->workspace_bytes, desc->workspace, p.ws_bytes);
+        if (reinterpret_cast<uintptr_t>(desc->workspace) % kAlign)
+            return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    }
+
+    dflash::AttnArgs& a = call->args;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k_pages = static_cast<const uint16_t*>(k_pages);
+    a.v_pages = static_cast<const uint16_t*>(v_pages);
+    a.page_table = page_table;
+    a.ctx_lens = ctx_lens;
+    a.block_lens = block_lens;
+    a.causal = causal;
+    a.out = static_cast<uint16_t*>(out);
+    a.part_o = p.ws_bytes ? static_cast<float*>(desc->workspace) : nullptr;
+    a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(desc->workspace) + p.off_lse) : nullptr;
+    a.d.B = desc->num_reqs;
+    a.d.Hkv = n_kv_heads;
+    a.d.G = n_heads / n_kv_heads;
+    a.d.window = window;
+    a.d.rmax = p.rmax;
+    a.d.tk = p.tk;
+    a.d.P = p.P;
+    a.Hq = n_heads;
+    a.D = head_dim;
+    a.Dp = p.Dp;
+    a.page_shift = ilog2(desc->page_size);
+    a.max_pages_per_req = desc->max_pages_per_req;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return DFLASH_OK;
+}
+
+int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t s)
+{
+    const Plan& p = call.plan;
+    const dflash::AttnArgs& a = call.args;
+    if (desc->event_attn_begin && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_begin), s) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_begin) failed");
+    hipError_t e = p.kernel == DFLASH_KERNEL_MFMA ? dflash::launch_attn_mfma(a, p.Dp, p.row_tiles, s)
+                                                  : dflash::launch_attn_ref(a, s);
+    if (e != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+    if (desc->event_attn_end && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_end), s) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_end) failed");
+    if (p.combine_wgs > 0) {
+        dflash::CombineArgs c;
+        c.ctx_lens = a.ctx_lens;
+        c.block_lens = a.block_lens;
+        c.part_o = a.part_o;
+        c.part_lse = a.part_lse;
+        c.out = a.out;
+        c.d = a.d;
+        c.Hq = a.Hq;
+        c.D = a.D;
+        c.Dp = p.Dp;
+        c.total_rows = (int64_t)desc->total_q * a.Hq;
+        e = dflash::launch_combine(c, p.combine_wgs, s);
+        if (e != hipSuccess)
+            return fail(DFLASH_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return DFLASH_OK;
+}
+
+int append_prepare(const void* k_new, const void* v_new, void* k_pages, void* v_pages, const int32_t* page_table,
+                   const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_kv_heads, int32_t head_dim,
+                   const dflash_batch_desc* desc, dflash::AppendArgs* a)
+{
+    if (!desc)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "desc is NULL");
+    int st = check_shape(n_kv_heads, n_kv_heads, head_dim);
+    if (st != DFLASH_OK)
+        return st;
+    if (desc->num_reqs < 0 || desc->total_q < 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "negative count in desc (num_reqs %d, total_q %d)", desc->num_reqs,
+                    desc->total_q);
+    if (!is_pow2(desc->page_size) || desc->page_size > 1024)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "page_size %d must be a power of two in [1, 1024]", desc->page_size);
+    if (desc->max_pages_per_req < 1)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "max_pages_per_req %d must be >= 1", desc->max_pages_per_req);
+    a->total_rows = (desc->num_reqs == 0) ? 0 : (int64_t)desc->total_q * n_kv_heads;
+    if (a->total_rows == 0)
+        return DFLASH_OK;
+    if (!k_new || !v_new || !k_pages || !v_pages || !page_table || !ctx_lens || !block_lens)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "NULL device pointer (k_new %p, v_new %p, k_pages %p, v_pages %p, "
+                    "page_table %p, ctx_lens %p, block_lens %p)", k_new, v_new, k_pages, v_pages, page_table,
+                    ctx_lens, block_lens);
+    auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
+    if (mis16(k_new) || mis16(v_new) || mis16(k_pages) || mis16(v_pages))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "k_new, v_new, k_pages and v_pages must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(block_lens) & 3u))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "page_table, ctx_lens and block_lens must be 4-byte aligned");
+    a->k_new = static_cast<const uint16_t*>(k_new);
+    a->v_new = static_cast<const uint16_t*>(v_new);
+    a->k_pages = static_cast<uint16_t*>(k_pages);
+    a->v_pages = static_cast<uint16_t*>(v_pages);
+    a->page_table = page_table;
+    a->ctx_lens = ctx_lens;
+    a->block_lens = block_lens;
+    a->B = desc->num_reqs;
+    a->Hkv = n_kv_heads;
+    a->D = head_dim;
+    a->page_shift = ilog2(desc->page_size);
+    a->max_pages_per_req = desc->max_pages_per_req;
+    return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,82 +411,54 @@ int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, c
                       int32_t head_dim, const uint8_t* causal, int32_t window, float scale, void* out,
                       void* stream, const dflash_batch_desc* desc)
 {
-    Plan p;
-    int st = make_plan(desc, n_heads, n_kv_heads, head_dim, &p);
+    AttnCall c;
+    const int st = attn_prepare(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads, n_kv_heads, head_dim,
+                                causal, window, scale, out, desc, &c);
+    if (st != DFLASH_OK || c.plan.empty)
+        return st;
+    return attn_launch(c, desc, static_cast<hipStream_t>(stream));
+}
+
+int dflash_block_kv_append(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                           const int32_t* page_table, const int32_t* ctx_lens, const int32_t* block_lens,
+                           int32_t n_kv_heads, int32_t head_dim, void* stream, const dflash_batch_desc* desc)
+{
+    dflash::AppendArgs a;
+    const int st = append_prepare(k_new, v_new, k_pages, v_pages, page_table, ctx_lens, block_lens, n_kv_heads,
+                                  head_dim, desc, &a);
+    if (st != DFLASH_OK || a.total_rows == 0)
+        return st;
+    const hipError_t e = dflash::launch_kv_append(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
+    return DFLASH_OK;
+}
+
+int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                             const int32_t* page_table, const int32_t* ctx_lens, const int32_t* block_lens,
+                             int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, const uint8_t* causal,
+                             int32_t window, float scale, void* out, void* stream, const dflash_batch_desc* desc)
+{
+    // both halves are validated before either is enqueued
+    dflash::AppendArgs ap;
+    int st = append_prepare(k_new, v_new, k_pages, v_pages, page_table, ctx_lens, block_lens, n_kv_heads, head_dim,
+                            desc, &ap);
     if (st != DFLASH_OK)
         return st;
-    if (!std::isfinite(scale))
-        return fail(DFLASH_ERR_INVALID_ARGUMENT, "scale must be finite");
-    if (p.empty)
-        return DFLASH_OK;
-    if (!q || !k_pages || !v_pages || !page_table || !ctx_lens || !block_lens || !out)
-        return fail(DFLASH_ERR_INVALID_ARGUMENT, "NULL device pointer (q %p, k_pages %p, v_pages %p, page_table %p, "
-                    "ctx_lens %p, block_lens %p, out %p)", q, k_pages, v_pages, page_table, ctx_lens, block_lens, out);
-    auto mis16 = [](const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) != 0; };
-    if (mis16(q) || mis16(k_pages) || mis16(v_pages) || mis16(out))
-        return fail(DFLASH_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(ctx_lens) & 3u) ||
-        (reinterpret_cast<uintptr_t>(block_lens) & 3u))
-        return fail(DFLASH_ERR_INVALID_ARGUMENT, "page_table, ctx_lens and block_lens must be 4-byte aligned");
-    if (p.ws_bytes > 0) {
-        if (!desc->workspace || desc->workspace_bytes < p.ws_bytes)
-            return fail(DFLASH_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes at %p; this call needs %zu bytes",
-                        desc->workspace_bytes, desc->workspace, p.ws_bytes);
-        if (reinterpret_cast<uintptr_t>(desc->workspace) % kAlign)
-            return fail(DFLASH_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
-    }
-
-    dflash::AttnArgs a;
-    a.q = static_cast<const uint16_t*>(q);
-    a.k_pages = static_cast<const uint16_t*>(k_pages);
-    a.v_pages = static_cast<const uint16_t*>(v_pages);
-    a.page_table = page_table;
-    a.ctx_lens = ctx_lens;
-    a.block_lens = block_lens;
-    a.causal = causal;
-    a.out = static_cast<uint16_t*>(out);
-    a.part_o = p.ws_bytes ? static_cast<float*>(desc->workspace) : nullptr;
-    a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(desc->workspace) + p.off_lse) : nullptr;
-    a.d.B = desc->num_reqs;
-    a.d.Hkv = n_kv_heads;
-    a.d.G = n_heads / n_kv_heads;
-    a.d.window = window;
-    a.d.rmax = p.rmax;
-    a.d.tk = p.tk;
-    a.d.P = p.P;
-    a.Hq = n_heads;
-    a.D = head_dim;
-    a.Dp = p.Dp;
-    a.page_shift = ilog2(desc->page_size);
-    a.max_pages_per_req = desc->max_pages_per_req;
-    a.scale_log2 = scale * 1.4426950408889634f;
-
+    AttnCall c;
+    st = attn_prepare(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads, n_kv_heads, head_dim, causal,
+                      window, scale, out, desc, &c);
+    if (st != DFLASH_OK)
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (desc->event_attn_begin && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_begin), s) != hipSuccess)
-        return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_begin) failed");
-    hipError_t e = p.kernel == DFLASH_KERNEL_MFMA ? dflash::launch_attn_mfma(a, p.Dp, p.row_tiles, s)
-                                                  : dflash::launch_attn_ref(a, s);
-    if (e != hipSuccess)
-        return fail(DFLASH_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
-    if (desc->event_attn_end && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_end), s) != hipSuccess)
-        return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_end) failed");
-    if (p.combine_wgs > 0) {
-        dflash::CombineArgs c;
-        c.ctx_lens = ctx_lens;
-        c.block_lens = block_lens;
-        c.part_o = a.part_o;
-        c.part_lse = a.part_lse;
-        c.out = a.out;
-        c.d = a.d;
-        c.Hq = n_heads;
-        c.D = head_dim;
-        c.Dp = p.Dp;
-        c.total_rows = (int64_t)desc->total_q * n_heads;
-        e = dflash::launch_combine(c, p.combine_wgs, s);
+    if (ap.total_rows > 0) {
+        const hipError_t e = dflash::launch_kv_append(ap, s);
         if (e != hipSuccess)
-            return fail(DFLASH_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
+            return fail(DFLASH_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
     }
-    return DFLASH_OK;
+    if (c.plan.empty)
+        return DFLASH_OK;
+    return attn_launch(c, desc, s);
 }
 
 }  // extern "C"

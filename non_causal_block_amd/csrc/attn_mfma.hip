@@ -35,6 +35,7 @@
 //    logits are masked, so their weight is exactly zero.
 //  * Epilogue: a unit finished inside the workgroup writes bf16 output;
 //    otherwise fp32 normalised partials + log2-sum-exp for combine.hip.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -643,18 +644,37 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
         walk(std::integral_constant<int, 1>{});
 }
 
+// Raises a kernel's dynamic-LDS limit once per device (not on every launch: a call
+// being captured into a graph then enqueues nothing but the launch itself).
+template <int DP, int RT, bool EXACT>
+static hipError_t ensure_lds_limit()
+{
+    using C = Cfg<DP, RT>;
+    if (C::LDS_BYTES <= 64 * 1024)
+        return hipSuccess;
+    static std::atomic<uint64_t> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit))
+        return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel<DP, RT, EXACT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    if (e == hipSuccess && bit)
+        done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
 template <int DP, int RT, bool EXACT>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
 {
     using C = Cfg<DP, RT>;
-    auto kern = attn_mfma_kernel<DP, RT, EXACT>;
-    if (C::LDS_BYTES > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-        if (e != hipSuccess)
-            return e;
-    }
-    hipLaunchKernelGGL(kern, dim3(a.d.P), dim3(C::THREADS), C::LDS_BYTES, stream, a);
+    const hipError_t e = ensure_lds_limit<DP, RT, EXACT>();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((attn_mfma_kernel<DP, RT, EXACT>), dim3(a.d.P), dim3(C::THREADS), C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
@@ -687,13 +707,20 @@ hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStrea
     }
 }
 
+// Resident workgroups per CU, queried once per kernel instance (the library runs on
+// one architecture, so the answer does not depend on the device).
 template <int DP, int RT, bool EXACT>
 static int occupancy_one()
 {
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT>, Cfg<DP, RT>::THREADS,
+    static std::atomic<int> cached{-1};
+    int blocks = cached.load(std::memory_order_acquire);
+    if (blocks >= 0)
+        return blocks;
+    if (ensure_lds_limit<DP, RT, EXACT>() != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT>, Cfg<DP, RT>::THREADS,
                                                      Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
         return 0;
+    cached.store(blocks, std::memory_order_release);
     return blocks;
 }
 

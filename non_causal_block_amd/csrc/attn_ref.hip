@@ -10,6 +10,8 @@
 // attention is needed" (non-causal block over context + block keys; causal =
 // self and left); vLLM PR #43445 report (per-request causal flag, sliding
 // window).
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -223,9 +225,13 @@ int ref_rows_per_unit() { return kRefRows; }
 
 int ref_wgs_per_cu()
 {
-    int blocks = 0;
+    static std::atomic<int> cached{-1};  // queried once (one architecture)
+    int blocks = cached.load(std::memory_order_acquire);
+    if (blocks >= 0)
+        return blocks;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_ref_kernel, kRefThreads, 0) != hipSuccess)
         return 0;
+    cached.store(blocks, std::memory_order_release);
     return blocks;
 }
 int ref_tile_keys() { return kRefTile; }

@@ -181,4 +181,20 @@ struct CombineArgs {
     int64_t total_rows;  // total_q hint * Hq
 };
 
+struct AppendArgs {
+    const uint16_t* k_new;  // bf16 [total_q][Hkv][D], block tokens in request order
+    const uint16_t* v_new;
+    uint16_t* k_pages;      // bf16 [num_pages][page][Hkv][D]
+    uint16_t* v_pages;
+    const int32_t* page_table;
+    const int32_t* ctx_lens;
+    const int32_t* block_lens;
+    int32_t B;
+    int32_t Hkv;
+    int32_t D;
+    int32_t page_shift;
+    int32_t max_pages_per_req;
+    int64_t total_rows;  // total_q * Hkv
+};
+
 }  // namespace dflash

@@ -24,6 +24,10 @@ int mfma_wgs_per_cu(int dpad, int row_tiles, bool exact);  // on the current dev
 int combine_grid(int64_t total_rows);
 hipError_t launch_combine(const CombineArgs& a, int grid, hipStream_t stream);
 
+// block K/V rows -> their pages (one wave per (token, kv-head) row)
+int append_grid(int64_t total_rows);
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+
 // streaming read of bytes (a multiple of 16) with grid workgroups, XOR of all words into *sink
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t stream);
 

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -85,6 +85,33 @@ def expect(status, want, fragment=""):
 def test_null_desc(lib):
     st = lib.dflash_block_attn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4, 512, None, 0, 1.0, FAKE, None, None)
     expect(st, nb.DFLASH_ERR_INVALID_ARGUMENT, "desc")
+
+
+def test_append_rejects_before_launch(lib):
+    d = desc()
+    stream = None
+
+    def app(kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, pt=FAKE, ctx=FAKE, blk=FAKE, hkv=4, hd=512, dd=d):
+        return nb.dflash_block_kv_append(kn, vn, kp, vp, pt, ctx, blk, hkv, hd, stream, dd)
+
+    expect(app(hd=520), nb.DFLASH_ERR_UNSUPPORTED, "512")
+    expect(app(hd=12), nb.DFLASH_ERR_UNSUPPORTED, "multiple of 8")
+    expect(app(hkv=0), nb.DFLASH_ERR_INVALID_ARGUMENT)
+    expect(app(kn=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    expect(app(vp=FAKE + 8), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    expect(app(blk=FAKE + 2), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    expect(app(dd=desc(page_size=12)), nb.DFLASH_ERR_INVALID_ARGUMENT, "page_size")
+    expect(lib.dflash_block_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, None, None),
+           nb.DFLASH_ERR_INVALID_ARGUMENT, "desc")
+    # nothing to append: OK without touching any pointer
+    expect(app(kn=0, vn=0, kp=0, vp=0, pt=0, ctx=0, blk=0, dd=desc(total_q=0)), nb.DFLASH_OK)
+    # the fused call validates both halves before enqueueing either: a bad append
+    # argument or a bad attention argument (no workspace) both fail up front
+    fused = lambda dd=d, kn=FAKE, scale=0.044: nb.dflash_block_attn_append(
+        FAKE, kn, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4, 512, None, 0, scale, FAKE, None, dd)
+    expect(fused(kn=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    expect(fused(scale=math.inf), nb.DFLASH_ERR_INVALID_ARGUMENT, "scale")
+    expect(fused(), nb.DFLASH_ERR_WORKSPACE_TOO_SMALL, "needs")
 
 
 def test_rejects_before_launch(lib):

@@ -237,6 +237,32 @@ def scatter_to_pages(logical: np.ndarray, kv_lens: np.ndarray, table: np.ndarray
     return pages
 
 
+def split_block_kv(wl: "Workload"):
+    """The block tokens' K/V rows and pages that hold only the context.
+
+    Returns (k_new, v_new, k_pages_ctx, v_pages_ctx): k_new / v_new are bf16 bits
+    [total_q, Hkv, D] -- row t is block token t - q_start[r] of its request,
+    packed in request order like q -- and the page arrays equal wl.k_pages /
+    wl.v_pages except that every block slot is NaN-poisoned (the state of the
+    cache before a draft step writes its block).
+    """
+    kv_start = wl.kv_start
+    rows = []
+    for r in range(wl.B):
+        L, n = int(wl.ctx_lens[r]), int(wl.block_lens[r])
+        rows.extend(range(int(kv_start[r]) + L, int(kv_start[r]) + L + n))
+    rows = np.asarray(rows, dtype=np.int64)
+    k_new = np.ascontiguousarray(wl.k[rows])
+    v_new = np.ascontiguousarray(wl.v[rows])
+    k_ctx = wl.k.copy()
+    v_ctx = wl.v.copy()
+    k_ctx[rows] = BF16_NAN
+    v_ctx[rows] = BF16_NAN
+    k_pages = scatter_to_pages(k_ctx, wl.kv_lens, wl.page_table, wl.num_pages, wl.page_size, True)
+    v_pages = scatter_to_pages(v_ctx, wl.kv_lens, wl.page_table, wl.num_pages, wl.page_size, True)
+    return k_new, v_new, k_pages, v_pages
+
+
 def build(B: int, Hq: int, Hkv: int, D: int, ctx_lens, block_lens, causal, *, window: int = 0,
           scale: Optional[float] = None, seed: int = 0, page_size: int = 16, permute_pages: bool = True,
           poison: bool = True, extra_pages: int = 0, name: str = "custom",
