@@ -16,6 +16,12 @@ K/V HBM bandwidth of the attention kernel against the 8 TB/s peak and against
 the measured streaming read, and the fp64 CPU oracle timed on a bounded sample
 of the same workload.
 
+    python bench.py --graph-latency
+measures one draft step (block K/V append + attention, one call) at the
+block-aligned capture sizes 9/18/36/72 (B = 1/2/4/8 requests x block 9) for
+the C1 and C2 request shapes, launched eagerly and as a replayed HIP graph;
+it prints its own JSON line instead of the throughput line.
+
     python bench.py --summarize-pmc FETCH_CSV WRITE_CSV
 turns two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE)
 into the HBM-traffic record the "traffic" field reads.
@@ -152,6 +158,90 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str) -> dict:
     }
 
 
+def graph_latency(reps: int = 200) -> dict:
+    """Per-call latency of dflash_block_attn_append, eager vs graph replay.
+
+    Each call is timed alone from the host (launch to completion, warm caches:
+    a draft step re-reads the context it just read) and on the GPU (events)."""
+    import numpy as np
+    import torch
+
+    import non_causal_block_amd as nb
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    shapes = {  # request shapes of C1 and C2 (block 9 = 1 + 8 speculative tokens)
+        "c1": dict(Hq=8, Hkv=2, D=128, ctx=lambda rng, B: np.full(B, 512)),
+        "c2": dict(Hq=32, Hkv=8, D=256, ctx=lambda rng, B: rng.integers(1024, 4097, size=B)),
+    }
+
+    def t16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    results = []
+    for name, sh in shapes.items():
+        for B in (1, 2, 4, 8):
+            rng = np.random.default_rng(2000 + B)
+            ctx = sh["ctx"](rng, B)
+            wl = workloads.build(B, sh["Hq"], sh["Hkv"], sh["D"], ctx, np.full(B, 9), np.zeros(B, dtype=np.uint8),
+                                 seed=2100 + B, poison=False)
+            k_new, v_new, kc, vc = workloads.split_block_kv(wl)
+            q, kn, vn, kp, vp = t16(wl.q), t16(k_new), t16(v_new), t16(kc), t16(vc)
+            pt, cl, bl = (torch.from_numpy(a).to(dev) for a in (wl.page_table, wl.ctx_lens, wl.block_lens))
+            out = torch.empty((wl.total_q, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+            desc = nb.make_desc(num_reqs=B, total_q=wl.total_q, max_block_len=9, total_kv_len=wl.total_kv,
+                                page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req,
+                                num_pages=wl.num_pages)
+            ws = torch.empty(max(nb.dflash_block_attn_workspace_size(desc, wl.Hq, wl.Hkv, wl.D), 256),
+                             dtype=torch.uint8, device=dev)
+            desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
+            plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
+            side = torch.cuda.Stream()
+
+            def call():
+                st = nb.dflash_block_attn_append(q, kn, vn, kp, vp, pt, cl, bl, wl.Hq, wl.Hkv, wl.D, None, 0,
+                                                 wl.scale, out, side.cuda_stream, desc)
+                if st != nb.DFLASH_OK:
+                    raise nb.DFlashError(st, nb.dflash_last_error_message())
+
+            with torch.cuda.stream(side):
+                for _ in range(10):
+                    call()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                call()
+            torch.cuda.synchronize()
+
+            def timed(fn):
+                host, gpu = [], []
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                for i in range(reps + 10):
+                    t0 = time.perf_counter()
+                    e0.record(side)
+                    fn()
+                    e1.record(side)
+                    side.synchronize()
+                    t1 = time.perf_counter()
+                    if i >= 10:
+                        host.append((t1 - t0) * 1e6)
+                        gpu.append(e0.elapsed_time(e1) * 1e3)
+                return float(np.median(host)), float(np.median(gpu))
+
+            with torch.cuda.stream(side):
+                eager_host, eager_gpu = timed(call)
+                graph_host, graph_gpu = timed(g.replay)
+            results.append({"shape": name, "B": B, "query_tokens": wl.total_q, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                            "head_dim": wl.D, "total_kv_tokens": wl.total_kv, "attn_workgroups": plan.num_workgroups,
+                            "combine": plan.combine_workgroups > 0,
+                            "eager_us": eager_host, "graph_us": graph_host,
+                            "eager_gpu_us": eager_gpu, "graph_gpu_us": graph_gpu})
+            print(f"[graph] {name} B={B}: eager {eager_host:.1f} us (gpu {eager_gpu:.1f}), "
+                  f"graph {graph_host:.1f} us (gpu {graph_gpu:.1f})", file=sys.stderr, flush=True)
+    return {"metric": "draft-step latency: block K/V append + attention, one call, us (median)",
+            "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": results}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +253,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--graph-latency", action="store_true")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
@@ -185,6 +276,11 @@ def main(argv=None) -> int:
 
     import non_causal_block_amd as nb
     import workloads
+
+    if args.graph_latency:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        print(json.dumps(graph_latency()), flush=True)
+        return 0
 
     if not os.path.exists(nb._lib.LIB_PATH):
         from non_causal_block_amd import build as hipbuild

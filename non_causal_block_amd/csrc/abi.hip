@@ -69,7 +69,11 @@ int device_cus(int* out)
     return DFLASH_OK;
 }
 
-constexpr int kMinTilesPerWg = 8;  // below this, fewer workgroups and fewer partials
+// Fewest key tiles per attention workgroup.  Small steps (a few requests of short
+// context) are latency-bound: a workgroup walks its tiles one after another, so
+// runs of one or two tiles (and a combine over more pieces) finish soonest;
+// large steps fill the chip long before this bound matters.
+constexpr int kMinTilesPerWg = 2;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

@@ -168,8 +168,8 @@ def test_plan_mfma_global_layer(lib):
 def test_plan_small_problem_uses_few_workgroups(lib):
     d = desc(num_reqs=1, total_q=9, total_kv_len=521, max_pages_per_req=33, num_pages=34)
     p = nb.dflash_block_attn_plan(d, 8, 2, 128)
-    # 17 tiles per kv-head, two kv-heads: a handful of workgroups, not the whole chip
-    assert 1 <= p.num_workgroups <= 8
+    # 17 tiles per kv-head, two kv-heads: two tiles per workgroup, not the whole chip
+    assert p.num_workgroups == 17
     assert p.head_dim_padded == 128 and p.rows_per_unit == 48
 
 
