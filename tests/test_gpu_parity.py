@@ -60,6 +60,15 @@ def test_c5_mixed_d512_reduced(kname, kernel):
     _full("c5_mixed_d512", kernel, ctx_cap=1500)
 
 
+# target-side verification on a hybrid model: local sliding-window and global layers
+def test_verify_local_window_d256():
+    _full("v_local_window_d256", nb.DFLASH_KERNEL_MFMA)
+
+
+def test_verify_global_d512():
+    _full("v_global_d512", nb.DFLASH_KERNEL_MFMA)
+
+
 def test_c5_mixed_d512_full_sampled():
     """Full-size mixed batch in the benchmark's launch configuration; the oracle
     computes a sample of rows: every row of the longest request, of a causal and of

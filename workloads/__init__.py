@@ -13,7 +13,8 @@ Shapes follow the pages' workloads:
     structure";
   * causal / sliding-window variants, vLLM PR #43445 report, "motivation".
 The five configurations below are the synthetic stand-ins for those
-workloads (GQA, bf16 values ~ N(0,1), paged KV with 16-token pages).
+workloads (GQA, bf16 values ~ N(0,1), paged KV with 16-token pages); two more
+(``v_*``) are the target's verification of the same blocks on a hybrid model.
 
 Recipe (fixed, so that every consumer sees identical arrays):
   numpy ``Generator(PCG64(seed))``; draw order lengths -> speculative token
@@ -96,6 +97,20 @@ CONFIGS = {
         "c5_mixed_d512", B=64, Hq=32, Hkv=8, D=512, ctx_law=("lognormal", 4096, 1.0, 256, 131072),
         spec_k=(4, 8, 15), causal_law=("bernoulli", 0.25),
         description="mixed batch B=64, k in {4,8,15}, lognormal L (median 4096), 25% causal, D 512, paged"),
+    # Target-side verification of the same blocks on a hybrid model: the verifier runs
+    # many local sliding-window layers and periodic global layers at head_dim 512
+    # (kenforever1 notes, "Gemma 4 31B-it structure"), each over the 1 + k block
+    # causally.  The pages give no window size or head counts: W = 1024 and the head
+    # counts of the configurations above are readings.
+    "v_local_window_d256": Config(
+        "v_local_window_d256", B=8, Hq=32, Hkv=8, D=256, ctx_law=("uniform", 8192, 32768), spec_k=(8,),
+        causal_law=("all", True), window=1024,
+        description="verify, local sliding-window layer: causal, W=1024, B=8 x block 9, L~U[8192,32768], "
+                    "Hq 32 / Hkv 8, D 256, paged"),
+    "v_global_d512": Config(
+        "v_global_d512", B=8, Hq=32, Hkv=4, D=512, ctx_law=("uniform", 8192, 32768), spec_k=(8,),
+        causal_law=("all", True),
+        description="verify, global layer: causal, B=8 x block 9, L~U[8192,32768], Hq 32 / Hkv 4, D 512, paged"),
 }
 CONFIG_ORDER = list(CONFIGS)
 SEED_BASE = 1000
