@@ -22,6 +22,10 @@ block-aligned capture sizes 9/18/36/72 (B = 1/2/4/8 requests x block 9) for
 the C1 and C2 request shapes, launched eagerly and as a replayed HIP graph;
 it prints its own JSON line instead of the throughput line.
 
+    python bench.py --conv
+times DFlash2's in-block grouped dynamic depthwise convolution (dflash_block_conv)
+at draft-step shapes and prints its own JSON line.
+
     python bench.py --summarize-pmc FETCH_CSV WRITE_CSV
 turns two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE)
 into the HBM-traffic record the "traffic" field reads.
@@ -242,6 +246,51 @@ def graph_latency(reps: int = 200) -> dict:
             "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": results}
 
 
+def conv_bench(reps: int = 200) -> dict:
+    """DFlash2 block convolution: GPU time per call and algorithmic bytes per second.
+
+    Shapes are readings (the pages give the formula, not the model sizes): blocks
+    of 1 + 15 positions, 5120 channels in 32 groups, 16 taps (the whole block)."""
+    import numpy as np
+    import torch
+
+    import non_causal_block_amd as nb
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    res = []
+    for B in (8, 64):
+        blocks = [16] * B
+        C, G, taps = 5120, 32, 16
+        x, base, delta = workloads.block_conv_inputs(blocks, C, G, taps, seed=3000 + B)
+
+        def t16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        tx, tb, td = t16(x), t16(base), t16(delta)
+        bl = torch.tensor(blocks, dtype=torch.int32, device=dev)
+        out = torch.empty_like(tx)
+        stream = torch.cuda.current_stream(dev)
+        for _ in range(10):
+            nb.block_conv(tx, tb, td, bl, groups=G, out=out)
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            e0[i].record(stream)
+            nb.block_conv(tx, tb, td, bl, groups=G, out=out)
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        us = float(np.median([e0[i].elapsed_time(e1[i]) * 1e3 for i in range(reps)]))
+        nbytes = (x.size + out.numel() + base.size + delta.size) * 2
+        res.append({"B": B, "block": 16, "channels": C, "groups": G, "taps": taps, "gpu_us": us,
+                    "algorithmic_bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
+                    "positions_per_s": B * 16 / (us * 1e-6)})
+        print(f"[conv] B={B}: {us:.1f} us, {nbytes/1e6:.1f} MB -> {nbytes/(us*1e-6)/1e9:.0f} GB/s",
+              file=sys.stderr, flush=True)
+    return {"metric": "DFlash2 in-block grouped dynamic depthwise convolution, GPU us per call (median)",
+            "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": res}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +303,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--graph-latency", action="store_true")
+    ap.add_argument("--conv", action="store_true")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
@@ -277,9 +327,9 @@ def main(argv=None) -> int:
     import non_causal_block_amd as nb
     import workloads
 
-    if args.graph_latency:
+    if args.graph_latency or args.conv:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
-        print(json.dumps(graph_latency()), flush=True)
+        print(json.dumps(graph_latency() if args.graph_latency else conv_bench()), flush=True)
         return 0
 
     if not os.path.exists(nb._lib.LIB_PATH):

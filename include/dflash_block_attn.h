@@ -179,6 +179,28 @@ const char* dflash_last_error_message(void);
 int dflash_abi_version(void);
 
 /*
+ * DFlash2 in-block grouped dynamic depthwise convolution (prhub summary of vLLM
+ * PR #52816, "DFlash2: local convolution + candidate selector", section
+ * "motivation"): for every request's block of n positions and every channel c,
+ *     out[i,c] = sum_{t=0}^{taps-1} (base[t,c] + delta[i,t,g(c)]) * x[i-t,c],
+ * where taps reaching before the block's first position (i - t < 0) are zero and
+ * g(c) = c / (channels / groups) (contiguous channel groups).
+ *   x      device bf16 [total_q, channels]; rows are block positions packed in
+ *          request order (request r: rows q_start[r] .. q_start[r] + n_r - 1)
+ *   base   device bf16 [taps, channels]
+ *   delta  device bf16 [total_q, taps, groups]
+ *   block_lens device int32 [num_reqs]; their sum must equal total_q
+ *   out    device bf16 [total_q, channels] (written; must not alias x)
+ * fp32 accumulation over t in increasing order, bf16 result rounded to nearest
+ * even.  channels even, groups dividing channels, 1 <= taps <= 1024,
+ * total_q <= 65535.  Host-checkable errors return before anything is
+ * enqueued; asynchronous on `stream`.
+ */
+int dflash_block_conv(const void* x, const void* base, const void* delta, const int32_t* block_lens,
+                       int32_t num_reqs, int32_t total_q, int32_t channels, int32_t groups, int32_t taps, void* out,
+                       void* stream);
+
+/*
  * Measurement helper, not part of the attention: reads `bytes` of device memory
  * at `buf` once, with the same streaming (nontemporal) 16-byte loads the
  * attention kernel uses for K/V, and XORs every 32-bit word it read into

@@ -48,6 +48,30 @@ def dflash_abi_version() -> int:
     return _lib.load().dflash_abi_version()
 
 
+def dflash_block_conv(x, base, delta, block_lens, num_reqs: int, total_q: int, channels: int, groups: int,
+                       taps: int, out, stream: Optional[int]) -> int:
+    """Raw call: DFlash2 in-block grouped dynamic depthwise convolution; status code out."""
+    return _lib.load().dflash_block_conv(_ptr(x), _ptr(base), _ptr(delta), _ptr(block_lens), num_reqs, total_q,
+                                          channels, groups, taps, _ptr(out), stream)
+
+
+def block_conv(x, base, delta, block_lens, *, groups: int, out=None):
+    """DFlash2 block convolution on torch device tensors (bf16); returns ``out``.
+
+    x: [total_q, C]; base: [taps, C]; delta: [total_q, taps, groups];
+    block_lens: int32 [B].  Runs on torch's current stream.
+    """
+    import torch
+
+    total_q, C = x.shape
+    taps = base.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _check(dflash_block_conv(x, base, delta, block_lens, block_lens.shape[0], total_q, C, groups, taps, out, stream))
+    return out
+
+
 def dflash_stream_read(buf, nbytes: int, sink, stream) -> int:
     """Measurement helper: one streaming read of nbytes at buf (see the C header)."""
     return _lib.load().dflash_stream_read(_ptr(buf), nbytes, _ptr(sink), stream)

@@ -90,6 +90,8 @@ def load() -> ctypes.CDLL:
     lib.dflash_block_attn_append.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, P, i32, ctypes.c_float, P, P,
                                              ctypes.POINTER(dflash_batch_desc)]
     lib.dflash_block_attn_append.restype = ctypes.c_int
+    lib.dflash_block_conv.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, P]
+    lib.dflash_block_conv.restype = ctypes.c_int
     lib.dflash_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.dflash_stream_read.restype = ctypes.c_int
     _lib = lib

@@ -334,6 +334,46 @@ extern "C" {
 
 int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
 
+int dflash_block_conv(const void* x, const void* base, const void* delta, const int32_t* block_lens,
+                       int32_t num_reqs, int32_t total_q, int32_t channels, int32_t groups, int32_t taps, void* out,
+                       void* stream)
+{
+    if (num_reqs < 0 || total_q < 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_conv: negative num_reqs (%d) or total_q (%d)", num_reqs, total_q);
+    if (total_q > 65535)
+        return fail(DFLASH_ERR_UNSUPPORTED, "block_conv: total_q %d > 65535 (one grid row per position)", total_q);
+    if (channels < 2 || channels % 2 != 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_conv: channels (%d) must be even and >= 2", channels);
+    if (groups < 1 || channels % groups != 0)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_conv: groups (%d) must divide channels (%d)", groups, channels);
+    if (taps < 1 || taps > 1024)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_conv: taps (%d) must be in [1, 1024]", taps);
+    if (num_reqs == 0 || total_q == 0)
+        return DFLASH_OK;
+    if (!x || !base || !delta || !block_lens || !out)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_conv: NULL device pointer");
+    if ((reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(base) & 3u) ||
+        (reinterpret_cast<uintptr_t>(out) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 1u) ||
+        (reinterpret_cast<uintptr_t>(block_lens) & 3u))
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "block_conv: x, base, out and block_lens must be 4-byte aligned, "
+                    "delta 2-byte aligned");
+    dflash::ConvArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.base = static_cast<const uint16_t*>(base);
+    a.delta = static_cast<const uint16_t*>(delta);
+    a.block_lens = block_lens;
+    a.out = static_cast<uint16_t*>(out);
+    a.B = num_reqs;
+    a.C = channels;
+    a.G = groups;
+    a.taps = taps;
+    a.total_rows = total_q;
+    const hipError_t e = dflash::launch_block_conv(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "block_conv launch failed: %s", hipGetErrorString(e));
+    return DFLASH_OK;
+}
+
 int dflash_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream)
 {
     if (bytes == 0)

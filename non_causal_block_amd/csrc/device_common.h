@@ -181,6 +181,19 @@ struct CombineArgs {
     int64_t total_rows;  // total_q hint * Hq
 };
 
+struct ConvArgs {
+    const uint16_t* x;      // bf16 [total_q][C]
+    const uint16_t* base;   // bf16 [taps][C]
+    const uint16_t* delta;  // bf16 [total_q][taps][G]
+    const int32_t* block_lens;
+    uint16_t* out;          // bf16 [total_q][C]
+    int32_t B;
+    int32_t C;
+    int32_t G;
+    int32_t taps;
+    int32_t total_rows;     // total_q (grid rows; rows past sum(block_lens) do nothing)
+};
+
 struct AppendArgs {
     const uint16_t* k_new;  // bf16 [total_q][Hkv][D], block tokens in request order
     const uint16_t* v_new;

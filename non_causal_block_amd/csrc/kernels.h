@@ -28,6 +28,9 @@ hipError_t launch_combine(const CombineArgs& a, int grid, hipStream_t stream);
 int append_grid(int64_t total_rows);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 
+// DFlash2 in-block grouped dynamic depthwise convolution
+hipError_t launch_block_conv(const ConvArgs& a, hipStream_t stream);
+
 // streaming read of bytes (a multiple of 16) with grid workgroups, XOR of all words into *sink
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t stream);
 

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -112,6 +112,20 @@ def test_append_rejects_before_launch(lib):
     expect(fused(kn=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
     expect(fused(scale=math.inf), nb.DFLASH_ERR_INVALID_ARGUMENT, "scale")
     expect(fused(), nb.DFLASH_ERR_WORKSPACE_TOO_SMALL, "needs")
+
+
+def test_block_conv_rejects_before_launch(lib):
+    def conv(x=FAKE, base=FAKE, delta=FAKE, blk=FAKE, B=4, total=36, C=4096, G=32, taps=16, out=FAKE):
+        return nb.dflash_block_conv(x, base, delta, blk, B, total, C, G, taps, out, None)
+
+    expect(conv(C=7), nb.DFLASH_ERR_INVALID_ARGUMENT, "even")
+    expect(conv(G=3), nb.DFLASH_ERR_INVALID_ARGUMENT, "divide")
+    expect(conv(taps=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "taps")
+    expect(conv(total=70000), nb.DFLASH_ERR_UNSUPPORTED, "65535")
+    expect(conv(B=-1), nb.DFLASH_ERR_INVALID_ARGUMENT, "negative")
+    expect(conv(x=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    expect(conv(out=FAKE + 2), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    expect(conv(x=0, base=0, delta=0, blk=0, out=0, total=0), nb.DFLASH_OK)  # nothing to do
 
 
 def test_rejects_before_launch(lib):

@@ -252,6 +252,23 @@ def scatter_to_pages(logical: np.ndarray, kv_lens: np.ndarray, table: np.ndarray
     return pages
 
 
+def block_conv_inputs(block_lens, channels: int, groups: int, taps: int, seed: int):
+    """Seeded inputs of DFlash2's in-block convolution, as bf16 bits.
+
+    x ~ N(0, 1) [total_q, channels]; base ~ N(0, 1/taps) [taps, channels] and
+    delta ~ N(0, 1/taps) [total_q, taps, groups] (so an output sums taps terms of
+    unit-order size); draw order x -> base -> delta.  The scales are readings: the
+    page gives the formula, not the coefficient statistics.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    total_q = int(np.sum(block_lens))
+    x = f32_to_bf16_bits(rng.standard_normal((total_q, channels), dtype=np.float32))
+    s = np.float32(1.0 / math.sqrt(taps))
+    base = f32_to_bf16_bits(rng.standard_normal((taps, channels), dtype=np.float32) * s)
+    delta = f32_to_bf16_bits(rng.standard_normal((total_q, taps, groups), dtype=np.float32) * s)
+    return x, base, delta
+
+
 def split_block_kv(wl: "Workload"):
     """The block tokens' K/V rows and pages that hold only the context.
 
