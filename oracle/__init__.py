@@ -42,6 +42,11 @@ def bind(path: str):
     f.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_int32, ctypes.c_double, P, ctypes.c_int64, P, ctypes.c_int32]
     f.restype = ctypes.c_int
+    if hasattr(lib, "oracle_block_attn_spans_f64"):
+        g = lib.oracle_block_attn_spans_f64
+        g.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                      ctypes.c_int32, ctypes.c_double, P, ctypes.c_int64, P, ctypes.c_int32]
+        g.restype = ctypes.c_int
     return lib
 
 
@@ -68,7 +73,7 @@ def _ptr(a: Optional[np.ndarray]):
 def block_attn_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_lens, block_lens, causal,
                    Hq: int, Hkv: int, D: int, window: int, scale: float,
                    rows: Optional[Sequence[int]] = None, threads: Optional[int] = None,
-                   lib=None) -> np.ndarray:
+                   lib=None, spans=None) -> np.ndarray:
     """Exact attention in fp64.
 
     q: uint16 bf16 bits [total_q, Hq, D]; k, v: uint16 [total_kv, Hkv, D] (logical,
@@ -76,6 +81,8 @@ def block_attn_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_lens, block_
     non-causal).  Returns float64 [total_q, Hq, D], or [len(rows), D] when ``rows``
     lists packed (token * Hq + head) indices.  ``lib`` selects another build of
     the same source (tests use it to check that the pins catch planted mistakes).
+    ``spans``: optional bidirectional spans, a per-request list of (start, end)
+    key-position pairs (sorted, disjoint), see oracle_f64.c.
     """
     lib = _load() if lib is None else lib
     q = np.ascontiguousarray(q, dtype=np.uint16)
@@ -97,14 +104,33 @@ def block_attn_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, ctx_lens, block_
         nr = int(rr.shape[0])
         out = np.empty((nr, D), dtype=np.float64)
     th = default_threads() if threads is None else int(threads)
-    rc = lib.oracle_block_attn_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(ctx), _ptr(blk), _ptr(cz), B, Hq, Hkv, D,
-                                   int(window), float(scale), _ptr(rr), nr, _ptr(out), th)
+    if spans is None:
+        rc = lib.oracle_block_attn_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(ctx), _ptr(blk), _ptr(cz), B, Hq, Hkv, D,
+                                       int(window), float(scale), _ptr(rr), nr, _ptr(out), th)
+    else:
+        offs, flat = spans_csr(spans, B)
+        rc = lib.oracle_block_attn_spans_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(ctx), _ptr(blk), _ptr(cz), _ptr(offs),
+                                             _ptr(flat), B, Hq, Hkv, D, int(window), float(scale), _ptr(rr), nr,
+                                             _ptr(out), th)
     if rc != 0:
         raise RuntimeError(f"oracle_block_attn_f64 failed with code {rc}")
     return out
 
 
-def run_workload(wl, rows: Optional[Sequence[int]] = None, threads: Optional[int] = None) -> np.ndarray:
+def spans_csr(spans, B: int):
+    """Per-request span lists -> (offsets int32 [B+1], pairs int32 [num_spans, 2])."""
+    offs = np.zeros(B + 1, dtype=np.int32)
+    flat = []
+    for r in range(B):
+        lst = list(spans[r]) if r < len(spans) else []
+        offs[r + 1] = offs[r] + len(lst)
+        flat.extend(lst)
+    pairs = np.asarray(flat, dtype=np.int32).reshape(-1, 2) if flat else np.zeros((1, 2), dtype=np.int32)
+    return offs, np.ascontiguousarray(pairs)
+
+
+def run_workload(wl, rows: Optional[Sequence[int]] = None, threads: Optional[int] = None,
+                 spans=None) -> np.ndarray:
     """Oracle output for a ``workloads.Workload`` (uses its logical K/V)."""
     return block_attn_f64(wl.q, wl.k, wl.v, wl.ctx_lens, wl.block_lens, wl.causal, wl.Hq, wl.Hkv, wl.D,
-                          wl.window, wl.scale, rows=rows, threads=threads)
+                          wl.window, wl.scale, rows=rows, threads=threads, spans=spans)

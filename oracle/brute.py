@@ -22,25 +22,30 @@ import math
 import numpy as np
 
 
-def visible(L: int, n: int, is_causal: bool, window: int, i: int, j: int) -> bool:
-    """Whether query i of a block (context L, block n) may attend to key j."""
+def visible(L: int, n: int, is_causal: bool, window: int, i: int, j: int, spans=()) -> bool:
+    """Whether query i of a block (context L, block n) may attend to key j.
+
+    ``spans``: the request's bidirectional spans, (start, end) key-position
+    pairs: two positions inside one span see each other in both directions,
+    even in a causal request (the mm-prefix case)."""
     T = L + n
     pos = L + i                      # the query's own key position
     if not (0 <= j < T):
         return False
-    if is_causal and j > pos:        # nothing to the right of the query
+    together = any(s <= pos < e and s <= j < e for s, e in spans)
+    if is_causal and j > pos and not together:   # nothing to the right, except inside a span
         return False
     if window > 0 and pos - j >= window:   # only the W keys ending at pos
         return False
     return True
 
 
-def mask_matrix(L: int, n: int, is_causal: bool, window: int) -> np.ndarray:
-    return np.array([[visible(L, n, is_causal, window, i, j) for j in range(L + n)] for i in range(n)],
+def mask_matrix(L: int, n: int, is_causal: bool, window: int, spans=()) -> np.ndarray:
+    return np.array([[visible(L, n, is_causal, window, i, j, spans) for j in range(L + n)] for i in range(n)],
                     dtype=bool)
 
 
-def block_attn(q, k, v, ctx_lens, block_lens, causal, Hq, Hkv, D, window, scale):
+def block_attn(q, k, v, ctx_lens, block_lens, causal, Hq, Hkv, D, window, scale, spans=None):
     """q [total_q, Hq, D], k/v [total_kv, Hkv, D] as float64 arrays (bf16 values).
 
     Returns float64 [total_q, Hq, D].
@@ -56,7 +61,7 @@ def block_attn(q, k, v, ctx_lens, block_lens, causal, Hq, Hkv, D, window, scale)
         L, n = int(ctx_lens[r]), int(block_lens[r])
         c = bool(causal[r]) if causal is not None else False
         T = L + n
-        M = mask_matrix(L, n, c, window)
+        M = mask_matrix(L, n, c, window, () if spans is None else spans[r])
         for i in range(n):
             for h in range(Hq):
                 g = h // G

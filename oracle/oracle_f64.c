@@ -21,6 +21,14 @@
  *       keys ending at the query's position (the window bounds only the low
  *       side; for a non-causal request the high end stays T-1).
  *
+ *   Bidirectional spans (optional; the mm-prefix case of the same notes,
+ *   section "what MooreThreads/vllm-musa PR #52 did": a multimodal prefix is
+ *   seen as a whole while text stays causal): request r lists spans
+ *   [s, e) of key positions (span_offsets[r] .. span_offsets[r+1]-1 in
+ *   `spans`, sorted, disjoint).  A query of a causal request whose position p
+ *   lies in a span [s, e) also sees the keys of that span after it: the high
+ *   end becomes max(p, e-1).  Non-causal requests see every key anyway.
+ *
  *   For q-head h, the kv-head is g = h / (Hq/Hkv) (contiguous GQA groups).
  *   z_j = scale * sum_d q[i,h,d] k[j,g,d]       (d ascending)
  *   m   = max_j z_j ;  e_j = exp(z_j - m) ;  s = sum_j e_j   (j ascending)
@@ -50,6 +58,8 @@ typedef struct {
     const uint16_t *q, *k, *v;
     const int32_t *ctx_lens, *block_lens;
     const uint8_t *causal;
+    const int32_t *span_offsets; /* [B+1] or NULL */
+    const int32_t *spans;        /* [num_spans][2] (start, end) */
     int32_t B, Hq, Hkv, D, window;
     double scale;
     const int64_t *kv_start; /* [B] */
@@ -77,6 +87,13 @@ static void attend_one(const job_t *J, int64_t tok, int32_t h, double *o, double
     const int is_causal = J->causal ? (J->causal[r] != 0) : 0;
 
     int64_t hi = is_causal ? p : T - 1;
+    if (is_causal && J->span_offsets) {
+        for (int32_t w = J->span_offsets[r]; w < J->span_offsets[r + 1]; ++w) {
+            const int64_t s = J->spans[2 * w], e = J->spans[2 * w + 1];
+            if (s <= p && p < e && e - 1 > hi)
+                hi = e - 1;
+        }
+    }
     int64_t lo = 0;
     if (J->window > 0) {
         lo = p - (int64_t)J->window + 1;
@@ -153,11 +170,30 @@ static void *worker(void *arg)
  *   rows != NULL : out is [n_rows][D], row w = (token rows[w]/Hq, head rows[w]%Hq).
  * Returns 0 on success, -1 on invalid arguments, -2 on allocation failure.
  */
+int oracle_block_attn_spans_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const int32_t *ctx_lens, const int32_t *block_lens, const uint8_t *causal,
+                                const int32_t *span_offsets, const int32_t *spans,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t window, double scale,
+                                const int64_t *rows, int64_t n_rows, double *out, int32_t n_threads);
+
 int oracle_block_attn_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                           const int32_t *ctx_lens, const int32_t *block_lens, const uint8_t *causal,
                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t window, double scale,
                           const int64_t *rows, int64_t n_rows, double *out, int32_t n_threads)
 {
+    return oracle_block_attn_spans_f64(q, k, v, ctx_lens, block_lens, causal, NULL, NULL, B, Hq, Hkv, D, window,
+                                       scale, rows, n_rows, out, n_threads);
+}
+
+/* As oracle_block_attn_f64, with optional bidirectional spans (both NULL = none). */
+int oracle_block_attn_spans_f64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const int32_t *ctx_lens, const int32_t *block_lens, const uint8_t *causal,
+                                const int32_t *span_offsets, const int32_t *spans,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t window, double scale,
+                                const int64_t *rows, int64_t n_rows, double *out, int32_t n_threads)
+{
+    if ((span_offsets == NULL) != (spans == NULL))
+        return -1;
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || (Hq % Hkv) != 0 || !out)
         return -1;
     int64_t total_q = 0;
@@ -200,6 +236,8 @@ int oracle_block_attn_f64(const uint16_t *q, const uint16_t *k, const uint16_t *
     J.ctx_lens = ctx_lens;
     J.block_lens = block_lens;
     J.causal = causal;
+    J.span_offsets = span_offsets;
+    J.spans = spans;
     J.B = B;
     J.Hq = Hq;
     J.Hkv = Hkv;
