@@ -47,7 +47,7 @@ METRIC = "query-tokens/s + K/V HBM GB/s (% of peak) for block attention, 1 MI355
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_mfma_c3_global_d512.json")
 FLUSH_BYTES = 1 << 30
-KERNEL_SOURCES = ["attn_mfma.hip", "device_common.h", "decomp.h"]
+KERNEL_SOURCES = ["attn_mfma_kernel.h", "attn_mfma.hip", "device_common.h", "decomp.h"]
 
 
 def kernel_source_hash() -> str:

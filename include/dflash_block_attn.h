@@ -122,6 +122,30 @@ int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, c
                       void* stream, const dflash_batch_desc* desc);
 
 /*
+ * dflash_block_attn with bidirectional spans inside causal requests: the
+ * multimodal-prefix mask (kenforever1 "DFlash + Gemma 4 31B-it" notes, section
+ * on MooreThreads/vllm-musa PR #52: an image prefix is attended as a whole while
+ * text stays causal).  A query at position p of a causal request that lies in
+ * one of the request's spans [s, e) also sees the keys after it up to e - 1:
+ * its visible range becomes [lo, max(p, e - 1)] (lo from the window as before).
+ * Positions count keys of the request from 0 (context 0..L-1, block L..L+n-1).
+ *   span_offsets  device int32 [num_reqs + 1] or NULL (= dflash_block_attn):
+ *                 request r's spans are entries span_offsets[r] .. span_offsets[r+1]-1
+ *   spans         device int32 [num_spans][2], (start, end) pairs, end exclusive;
+ *                 may be NULL when num_spans == 0
+ *   num_spans     entries of `spans`; the kernels skip entries outside [0, num_spans)
+ * Spans of non-causal requests change nothing.  Spans may come in any order and
+ * may overlap (the largest end among those holding p counts); ranges are clipped
+ * to the request's keys.  Other arguments, errors and asynchrony as for
+ * dflash_block_attn; both span pointers must be 4-byte aligned.
+ */
+int dflash_block_attn_spans(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                            const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
+                            int32_t head_dim, const uint8_t* causal, const int32_t* span_offsets,
+                            const int32_t* spans, int32_t num_spans, int32_t window, float scale, void* out,
+                            void* stream, const dflash_batch_desc* desc);
+
+/*
  * Block K/V append: writes each request's block K/V into the paged cache, the
  * step that must precede the attention (the block's queries attend to the
  * context K/V together with the block's own K/V -- kenforever1 notes, "why

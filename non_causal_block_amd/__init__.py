@@ -111,6 +111,16 @@ def dflash_block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_h
                                          scale, _ptr(out), stream, ctypes.byref(desc))
 
 
+def dflash_block_attn_spans(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads: int, n_kv_heads: int,
+                            head_dim: int, causal, span_offsets, spans, num_spans: int, window: int, scale: float,
+                            out, stream: Optional[int], desc: dflash_batch_desc) -> int:
+    """Raw call with bidirectional spans in causal requests; status code out."""
+    return _lib.load().dflash_block_attn_spans(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table),
+                                               _ptr(ctx_lens), _ptr(block_lens), n_heads, n_kv_heads, head_dim,
+                                               _ptr(causal), _ptr(span_offsets), _ptr(spans), num_spans, window,
+                                               scale, _ptr(out), stream, ctypes.byref(desc))
+
+
 def dflash_block_kv_append(k_new, v_new, k_pages, v_pages, page_table, ctx_lens, block_lens, n_kv_heads: int,
                            head_dim: int, stream: Optional[int], desc: dflash_batch_desc) -> int:
     """Raw call: write the block K/V rows into their pages; status code out."""
@@ -149,13 +159,16 @@ def make_desc(*, num_reqs: int, total_q: int, max_block_len: int, total_kv_len: 
 
 def block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, *, causal=None, window: int = 0,
                scale: Optional[float] = None, out=None, max_block_len: int = 0, total_kv_len: int = 0,
-               kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0, workspace=None):
+               kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0, workspace=None, span_offsets=None,
+               spans=None):
     """Block attention on torch device tensors; returns ``out`` (bf16 [total_q, Hq, D]).
 
     q: bf16 [total_q, Hq, D]; k_pages/v_pages: bf16 [num_pages, page_size, Hkv, D];
     page_table: int32 [B, max_pages_per_req]; ctx_lens/block_lens: int32 [B];
     causal: uint8 [B] or None.  ``max_block_len``/``total_kv_len`` are host hints
-    (0 = unknown).  Runs on torch's current stream.
+    (0 = unknown).  ``span_offsets`` (int32 [B+1]) with ``spans`` (int32 [S, 2])
+    add bidirectional spans to causal requests (dflash_block_attn_spans).  Runs on
+    torch's current stream.
     """
     import torch
 
@@ -178,6 +191,12 @@ def block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, *, causal=
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if span_offsets is not None:
+        num_spans = 0 if spans is None else spans.shape[0]
+        _check(dflash_block_attn_spans(q, k_pages, v_pages, page_table, ctx_lens, block_lens, Hq, Hkv, D, causal,
+                                       span_offsets, spans if num_spans else None, num_spans, window, scale, out,
+                                       stream, desc))
+        return out
     _check(dflash_block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, Hq, Hkv, D, causal, window,
                              scale, out, stream, desc))
     return out

@@ -71,6 +71,9 @@ def load() -> ctypes.CDLL:
     lib.dflash_block_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, i32, ctypes.c_float, P, P,
                                       ctypes.POINTER(dflash_batch_desc)]
     lib.dflash_block_attn.restype = ctypes.c_int
+    lib.dflash_block_attn_spans.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P, P, i32, i32, ctypes.c_float, P,
+                                            P, ctypes.POINTER(dflash_batch_desc)]
+    lib.dflash_block_attn_spans.restype = ctypes.c_int
     lib.dflash_block_attn_workspace_size.argtypes = [ctypes.POINTER(dflash_batch_desc), i32, i32, i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.dflash_block_attn_workspace_size.restype = ctypes.c_int

@@ -198,8 +198,9 @@ struct AttnCall {
 
 int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
                  const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
-                 int32_t head_dim, const uint8_t* causal, int32_t window, float scale, void* out,
-                 const dflash_batch_desc* desc, AttnCall* call)
+                 int32_t head_dim, const uint8_t* causal, const int32_t* span_offsets, const int32_t* spans,
+                 int32_t num_spans, int32_t window, float scale, void* out, const dflash_batch_desc* desc,
+                 AttnCall* call)
 {
     Plan& p = call->plan;
     int st = make_plan(desc, n_heads, n_kv_heads, head_dim, &p);
@@ -207,6 +208,14 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
         return st;
     if (!std::isfinite(scale))
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (span_offsets) {
+        if (num_spans < 0)
+            return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_spans %d must be >= 0", num_spans);
+        if (num_spans > 0 && !spans)
+            return fail(DFLASH_ERR_INVALID_ARGUMENT, "spans is NULL with num_spans %d", num_spans);
+        if ((reinterpret_cast<uintptr_t>(span_offsets) & 3u) || (reinterpret_cast<uintptr_t>(spans) & 3u))
+            return fail(DFLASH_ERR_INVALID_ARGUMENT, "span_offsets and spans must be 4-byte aligned");
+    }
     if (p.empty)
         return DFLASH_OK;
     if (!q || !k_pages || !v_pages || !page_table || !ctx_lens || !block_lens || !out)
@@ -234,6 +243,9 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.ctx_lens = ctx_lens;
     a.block_lens = block_lens;
     a.causal = causal;
+    a.span_offsets = span_offsets;
+    a.spans = span_offsets ? spans : nullptr;
+    a.num_spans = span_offsets ? num_spans : 0;
     a.out = static_cast<uint16_t*>(out);
     a.part_o = p.ws_bytes ? static_cast<float*>(desc->workspace) : nullptr;
     a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(desc->workspace) + p.off_lse) : nullptr;
@@ -457,7 +469,21 @@ int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, c
 {
     AttnCall c;
     const int st = attn_prepare(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads, n_kv_heads, head_dim,
-                                causal, window, scale, out, desc, &c);
+                                causal, nullptr, nullptr, 0, window, scale, out, desc, &c);
+    if (st != DFLASH_OK || c.plan.empty)
+        return st;
+    return attn_launch(c, desc, static_cast<hipStream_t>(stream));
+}
+
+int dflash_block_attn_spans(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                            const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
+                            int32_t head_dim, const uint8_t* causal, const int32_t* span_offsets,
+                            const int32_t* spans, int32_t num_spans, int32_t window, float scale, void* out,
+                            void* stream, const dflash_batch_desc* desc)
+{
+    AttnCall c;
+    const int st = attn_prepare(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads, n_kv_heads, head_dim,
+                                causal, span_offsets, spans, num_spans, window, scale, out, desc, &c);
     if (st != DFLASH_OK || c.plan.empty)
         return st;
     return attn_launch(c, desc, static_cast<hipStream_t>(stream));
@@ -491,7 +517,7 @@ int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new
         return st;
     AttnCall c;
     st = attn_prepare(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads, n_kv_heads, head_dim, causal,
-                      window, scale, out, desc, &c);
+                      nullptr, nullptr, 0, window, scale, out, desc, &c);
     if (st != DFLASH_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -1,714 +1,22 @@
-// attn_mfma.hip -- the MFMA (matrix-core) block-attention kernel for gfx950.
-//
-// What it computes: kenforever1 "DFlash + Gemma 4 31B-it" notes, "why
-// non-causal attention is needed" -- each request's block of 1+k queries
-// attends, as a whole, to the context K/V plus the block's own K/V; the
-// causal variant lets query i see only itself and keys to its left; vLLM PR
-// #43445 (report, "implementation") makes causality a per-request flag and
-// adds sliding-window DFlash.  Global layers need head_dim 512 (notes,
-// "Gemma 4 31B-it structure").
-//
-// How (gfx950, wave64, 4 waves per workgroup, one wave per SIMD):
-//  * Work: decomp.h -- each workgroup takes an equal run of 32-key tiles over
-//    all (request, kv-head, row group) units; all G q-heads of a kv-head and
-//    all n block queries share every K/V byte (rows = n*G, tiled by 16).
-//  * The head dimension is split over the 4 waves (DW = Dp/4 each).  Wave w
-//    streams only its d-slice of every key: K straight from HBM into MFMA
-//    A-operand registers (8 consecutive d of one key per lane, 16-byte loads),
-//    V into registers and from there into a wave-private LDS tile.
-//  * S^T = K Q^T per wave over its d-slice with v_mfma_f32_16x16x32_bf16
-//    (A = K, rows = keys; B = Q^T, held for the whole unit); the four partial
-//    S^T tiles are summed through LDS by the wave that owns the row tile, which
-//    applies the mask, runs the softmax (exp2; max over lanes with
-//    xor-shuffles) and publishes P^T in exactly the MFMA B-operand layout.
-//  * O^T += V^T P^T per wave for its d-slice (A = V^T gathered from LDS, B =
-//    P^T from LDS), fp32 accumulators in registers.
-//  * No rescaling of the accumulators: a row's reference max is its first
-//    visible tile's max, kept while later tiles stay within 2^32 of it (the
-//    probabilities then fit bf16/fp32 comfortably).  A tile beyond that
-//    (extreme logit ranges only) abandons the segment; after its run the
-//    workgroup recomputes such segments with each row's exact max found by a
-//    K-only pass.  Numerator and denominator share the reference, so the
-//    result is the same softmax either way.
-//  * Keys past the request's end are read from the request's first visible key
-//    row instead, so page-tail garbage (possibly NaN) is never loaded; their
-//    logits are masked, so their weight is exactly zero.
-//  * Epilogue: a unit finished inside the workgroup writes bf16 output;
-//    otherwise fp32 normalised partials + log2-sum-exp for combine.hip.
-#include <atomic>
-#include <type_traits>
-
-#include "device_common.h"
-#include "kernels.h"
+// attn_mfma.hip -- instances of the MFMA block-attention kernel (attn_mfma_kernel.h)
+// for plain masks, the dispatch between plain and span instances, and the
+// occupancy queries the planner uses.
+#include "attn_mfma_kernel.h"
 
 namespace dflash {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Waves per workgroup: the head dimension is split over them (DP / WAVES d each).
-// Four, one per SIMD.  An 8-way split at head_dim 512 (two waves per SIMD, 80
-// accumulators each) passes the same tests but ran about 5% slower on C3: the
-// barriers keep both waves of a SIMD in the same phase, and each row-tile owner
-// then sums twice as many partial products.
-constexpr int waves_for(int /*dp*/) { return 4; }
-template <int DP>
-constexpr int threads_for = waves_for(DP) * 64;
-constexpr int kTK = 32;              // keys per tile (two 16-key MFMA tiles)
-constexpr float kLazyBound = 32.0f;  // log2 units a row max may exceed its reference by
-constexpr int kLazy = 0, kMaxScan = 1, kFixed = 2;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
-
-__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x4_t ldg16(const uint16_t* p)
-{
-    return *reinterpret_cast<const u32x4_t*>(p);
-}
-
-// K/V rows are read once per call: a streaming (nontemporal) load does not
-// allocate them in the caches, which keeps the last-level cache from evicting
-// (and writing back) other data on their account.
-__device__ __forceinline__ u32x4_t ldg16_stream(const uint16_t* p)
-{
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane 4q+r
-// receives element r of the 8-byte rows addressed by lanes q, q+4, q+8, q+12.
-__device__ __forceinline__ u32x2_t ds_read_tr16(const unsigned char* p)
-{
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
-    return __builtin_bit_cast(u32x2_t, v);
-}
-
-// Max over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the gfx950
-// row-swap instructions, which stay in the VALU instead of going through LDS.
-__device__ __forceinline__ float max_across_groups(float x)
-{
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    // gfx950 converts with v_cvt_pk_bf16_f32 (round to nearest even)
-    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-template <int DP, int RT>
-struct Cfg {
-    static constexpr int WAVES = waves_for(DP);
-    static constexpr int THREADS = WAVES * 64;
-    static constexpr int DW = DP / WAVES;  // d per wave
-    static constexpr int KS = DW / 32;      // QK^T k-steps per wave
-    static constexpr int DT = DW / 16;      // PV d-tiles per wave
-    static constexpr int ROWS = 16 * RT;
-    static constexpr int NOWN = (RT + WAVES - 1) / WAVES;  // row tiles owned per wave
-    // K/V loads: a key's d-slice is NCH 16-byte chunks, read by NCH consecutive lanes, so
-    // one load instruction covers KPI whole slices (256 contiguous bytes per key at
-    // head_dim 512); a 32-key tile takes NI loads each of K and V per wave.
-    static constexpr int NCH = DW / 8;
-    static constexpr int KPI = 64 / NCH;
-    static constexpr int NI = kTK / KPI;
-    static constexpr int KSH = NCH == 16 ? 0 : NCH == 8 ? 1 : 2;
-    // K tile, row-major [key][d_local] in 16-byte chunks; chunk c of row r sits at
-    // c ^ ((r >> KSH) % NCH), which keeps both the row-wise stores and the MFMA-order
-    // reads (16 keys at one chunk) free of bank conflicts.
-    static constexpr int KROW = DW * 2;
-    static __device__ __forceinline__ int kofs(int row, int chunk)
-    {
-        return row * KROW + 16 * (chunk ^ ((row >> KSH) & (NCH - 1)));
-    }
-    // V tile, row-major [key][d_local], addressed in 8-byte chunks.  A transposing
-    // read touches four key rows of 32 bytes per 16-lane group (eight rows per
-    // 32-lane pass).  Rows of 256 bytes XOR the chunk index with 4*(row % 8), which
-    // puts the eight rows of a pass on distinct banks; shorter rows get a 32-byte pad.
-    static constexpr bool VSWZ = DW * 2 == 256;
-    static constexpr int VROW = VSWZ ? DW * 2 : DW * 2 + 32;
-    static __device__ __forceinline__ int vofs(int row, int chunk)
-    {
-        return row * VROW + 8 * (VSWZ ? chunk ^ ((row & 7) << 2) : chunk);
-    }
-    // LDS layout (bytes)
-    static constexpr int SX_BYTES = WAVES * 2 * RT * 64 * 16;  // partial S^T [wave][h][b][lane]
-    static constexpr int PX_BYTES = RT * 64 * 16;               // P^T (B operand) [b][lane]
-    static constexpr int V_BYTES_PER_WAVE = kTK * VROW;
-    static constexpr int V_BYTES = WAVES * V_BYTES_PER_WAVE;
-    static constexpr int K_BYTES_PER_WAVE = kTK * KROW;
-    static constexpr int K_BYTES = WAVES * K_BYTES_PER_WAVE;
-    static constexpr int ROWF_BYTES = ROWS * 4;
-    static constexpr int OFF_SX = 0;
-    static constexpr int OFF_PX = OFF_SX + SX_BYTES;
-    static constexpr int OFF_V = OFF_PX + PX_BYTES;
-    static constexpr int OFF_K = OFF_V + V_BYTES;
-    static constexpr int OFF_LSUM = OFF_K + K_BYTES;
-    static constexpr int OFF_MREF = OFF_LSUM + ROWF_BYTES;
-    static constexpr int OFF_FLAG = OFF_MREF + ROWF_BYTES;
-    static constexpr int LDS_BYTES = OFF_FLAG + 16 * 4;
-    static_assert(KS >= 1 && DT >= 1, "head_dim too small for the d-split");
-    static_assert(NCH >= 4 && NCH <= 16 && KPI * NCH == 64 && NI * KPI == kTK, "load geometry");
-    static_assert(RT <= 16, "flag array");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-};
-
-// EXACT: head_dim == DP, so every d-chunk exists and no lane needs masking.
-template <int DP, int RT, bool EXACT>
-__global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
-{
-    using C = Cfg<DP, RT>;
-    constexpr int WAVES = C::WAVES;
-    constexpr int KS = C::KS;
-    constexpr int DT = C::DT;
-    constexpr int DW = C::DW;
-    constexpr int NOWN = C::NOWN;
-
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    f32x4_t* sx = reinterpret_cast<f32x4_t*>(lds + C::OFF_SX);
-    u32x4_t* px = reinterpret_cast<u32x4_t*>(lds + C::OFF_PX);
-    float* lsum_s = reinterpret_cast<float*>(lds + C::OFF_LSUM);
-    float* mref_s = reinterpret_cast<float*>(lds + C::OFF_MREF);
-    int* flag_s = reinterpret_cast<int*>(lds + C::OFF_FLAG);
-
-    const Decomp& d = a.d;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15;
-    const int grp4 = lane >> 4;
-    const int wbase = wave * DW;  // first d of this wave's slice
-    unsigned char* vls = lds + C::OFF_V + wave * C::V_BYTES_PER_WAVE;
-    unsigned char* kls = lds + C::OFF_K + wave * C::K_BYTES_PER_WAVE;
-    constexpr int NI = C::NI;
-    constexpr int KPI = C::KPI;
-    const int kl = lane / C::NCH;  // key of this lane within a load's KPI keys
-    const int sl = lane % C::NCH;  // 16-byte chunk of this lane within the key's d-slice
-    // this lane's chunk exists (always, unless head_dim < padded head_dim); an absent one
-    // reads the row start, finite data that meets a zero Q chunk or an unstored column
-    const bool lval = EXACT || wbase + 8 * sl < a.D;
-
-    const int32_t wg = logical_wg(blockIdx.x, d.P);
-    const int32_t D = a.D;
-    const int32_t G = d.G;
-    const int32_t psize = 1 << a.page_shift;
-
-    // d-chunks of this lane that exist (all of them unless head_dim < padded head_dim)
-    bool dval[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-        dval[s] = EXACT || (wbase + 32 * s + 8 * grp4 < D);
-
-    const int64_t total = wave_total_work(a.ctx_lens, a.block_lens, d);
-    const int64_t tpw = tiles_per_wg(total, d.P);
-    const int64_t begin = (int64_t)wg * tpw;
-    const int64_t end = min(total, begin + tpw);
-    if (begin >= end)
-        return;
-
-    int32_t r_first;
-    int64_t rbase_first;
-    wave_find_request(a.ctx_lens, a.block_lens, d, begin, r_first, rbase_first);
-    int64_t qstart_first = 0;  // first query token of request r_first
-    for (int32_t base = 0; base < r_first; base += 64) {
-        int64_t nn = (base + lane < r_first) ? (int64_t)a.block_lens[base + lane] : 0;
-        qstart_first += shfl_i64(wave_inclusive_scan(nn), 63);
-    }
-
-    // Segments of this workgroup's run that a lazy pass abandoned (bit i: i-th segment;
-    // segments past 63 share the overflow flag and are all recomputed).
-    uint64_t redo_mask = 0;
-    bool redo_overflow = false;
-
-    f32x4_t o[DT][RT];
-    float m_run[NOWN];
-    float l_run[NOWN];
-
-    // Walks the run; phase 0 runs every segment lazily, phase 1 recomputes abandoned ones.
-    auto walk = [&](auto phase_tag) {
-        constexpr int PHASE = decltype(phase_tag)::value;
-        int32_t r = r_first;
-        int64_t rbase = rbase_first;
-        int64_t qstart = qstart_first;
-        int64_t pos = begin;
-        int seg = 0;
-        while (pos < end) {
-            const int32_t L = a.ctx_lens[r];
-            const int32_t n = a.block_lens[r];
-            const ReqGeom g = req_geom(L, n, d);
-            const int64_t w = req_work(g, d);
-            if (pos >= rbase + w) {
-                rbase += w;
-                qstart += n;
-                ++r;
-                continue;
-            }
-            const int64_t off = pos - rbase;
-            const int32_t unit = (int32_t)(off / g.ntiles);
-            // segment bounds are wave-uniform; readfirstlane lets the compiler keep the tile
-            // loop in scalar control flow with exact memory-counter waits
-            const int32_t t0 = __builtin_amdgcn_readfirstlane((int32_t)(off % g.ntiles));
-            const int64_t seg_end = min(end, rbase + (int64_t)(unit + 1) * g.ntiles);
-            const int32_t t1 = __builtin_amdgcn_readfirstlane((int32_t)(seg_end - rbase - (int64_t)unit * g.ntiles));
-            const int this_seg = seg++;
-            pos = seg_end;
-            if constexpr (PHASE == 1) {
-                const bool redo = this_seg < 64 ? ((redo_mask >> this_seg) & 1u) != 0 : redo_overflow;
-                if (!redo)
-                    continue;
-            }
-            const int32_t kvh = unit / g.ngroups;
-            const int32_t grp = unit % g.ngroups;
-            const int slot = (this_seg == 0) ? 0 : 1;
-            const bool whole = (t0 == 0 && t1 == g.ntiles);
-            const bool is_causal = a.causal ? (a.causal[r] != 0) : false;
-            const int32_t row0 = grp * d.rmax;
-            const int32_t rows_here = min(d.rmax, n * G - row0);
-            const int32_t T = g.T;
-            const int32_t* pt = a.page_table + (int64_t)r * a.max_pages_per_req;
-            // element offset of kv-head kvh inside a key row; d-chunks past head_dim
-            // address the row start instead (never past the row), and are zeroed
-            const int64_t head_off = (int64_t)kvh * D;
-
-            // ---------------- Q^T (B operand) for the unit ----------------
-            bf16x8_t qf[RT][KS];
-#pragma unroll
-            for (int b = 0; b < RT; ++b) {
-                const int32_t row = b * 16 + l16;
-                const bool rv = row < rows_here;
-                const int32_t rr = row0 + (rv ? row : 0);
-                const int32_t qi = rr / G;
-                const int32_t qj = rr % G;
-                const uint16_t* qrow = a.q + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    u32x4_t x = ldg16(qrow + (dval[s] ? wbase + 32 * s + 8 * grp4 : 0));
-                    const bool keep = rv && dval[s];
-                    x[0] = keep ? x[0] : 0u;
-                    x[1] = keep ? x[1] : 0u;
-                    x[2] = keep ? x[2] : 0u;
-                    x[3] = keep ? x[3] : 0u;
-                    qf[b][s] = as_bf16x8(x);
-                }
-            }
-
-            // Element offset of the request's first visible key row: keys past the end (and
-            // tiles past the segment) read it, so every load stays in bounds and finite.
-            const int64_t safe_row =
-                ((int64_t)pt[g.kv_lo >> a.page_shift] * psize + (g.kv_lo & (psize - 1))) * d.Hkv * (int64_t)D;
-            // Tile keys are located in two steps so that no wait lands on loads in flight:
-            // tile_page() reads, one tile ahead, the page-table entry of key lane % 32 of the
-            // tile (at a clamped, always valid index); tile_rows() hands each lane the
-            // entries of its NI keys when the tile's K/V are requested -- two lane reads when
-            // a page spans 16 keys, else a shuffle per key.  Keys past the end and tiles
-            // past the segment get the safe row.
-            auto tile_page = [&](int32_t t) -> int32_t {
-                const int32_t key = g.kv_lo + t * kTK + (lane & 31);
-                return pt[(key < T ? key : T - 1) >> a.page_shift];
-            };
-            const int32_t hkvd = d.Hkv * D;  // elements per key row
-            auto tile_rows = [&](int32_t t, int32_t pgl, int64_t (&rows)[NI]) {
-                const int32_t k0 = g.kv_lo + t * kTK;
-                // keys at or past kend read the safe row (kend = 0 for a tile past the segment)
-                const int32_t kend = t < t1 ? T : 0;
-                int32_t page[NI];
-                if (a.page_shift >= 4) {
-                    const int32_t p0 = __builtin_amdgcn_readlane(pgl, 0);
-                    const int32_t p1 = __builtin_amdgcn_readlane(pgl, 16);
-#pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        page[i] = (i * KPI) & 16 ? p1 : p0;
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        page[i] = __builtin_amdgcn_ds_bpermute(4 * (i * KPI + kl), pgl);
-                }
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    const int32_t key = k0 + i * KPI + kl;
-                    const uint64_t slot = (uint64_t)(uint32_t)page[i] * (uint32_t)psize + (uint32_t)(key & (psize - 1));
-                    const int64_t row = (int64_t)(slot * (uint32_t)hkvd);
-                    rows[i] = key < kend ? row : safe_row;
-                }
-            };
-
-            float m_fix[NOWN];
-            // Visible key range [rlo, rhi] of this lane's query row in each owned row tile, and
-            // the keys [ilo, ihi] every real row of the tile sees: a tile inside that range
-            // needs no mask (padding rows then get finite weights that reach no output).
-            int32_t rlo[NOWN], rhi[NOWN], ilo[NOWN], ihi[NOWN];
-#pragma unroll
-            for (int ob = 0; ob < NOWN; ++ob) {
-                m_fix[ob] = -INFINITY;
-                const int32_t row = (ob * WAVES + wave) * 16 + l16;
-                const bool rv = row < rows_here;
-                query_range(L, n, (row0 + (rv ? row : 0)) / G, is_causal, d.window, rlo[ob], rhi[ob]);
-                int32_t lo_all = rv ? rlo[ob] : INT32_MIN;
-                int32_t hi_all = rv ? rhi[ob] : INT32_MAX;
-                if (!rv)
-                    rhi[ob] = -1;  // padding row: nothing visible
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) {
-                    lo_all = max(lo_all, __shfl_xor(lo_all, off));
-                    hi_all = min(hi_all, __shfl_xor(hi_all, off));
-                }
-                ilo[ob] = __builtin_amdgcn_readfirstlane(lo_all);
-                ihi[ob] = __builtin_amdgcn_readfirstlane(hi_all);
-            }
-
-            // One pass over the segment's tiles (MODE kLazy, kMaxScan or kFixed).  Returns
-            // true when a kLazy pass met a tile beyond its reference bound.
-            auto run_pass = [&](auto mode_tag) -> bool {
-                constexpr int MODE = decltype(mode_tag)::value;
-                if constexpr (MODE != kMaxScan) {
-#pragma unroll
-                    for (int c = 0; c < DT; ++c)
-#pragma unroll
-                        for (int b = 0; b < RT; ++b)
-                            o[c][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int ob = 0; ob < NOWN; ++ob) {
-                    m_run[ob] = MODE == kFixed ? m_fix[ob] : -INFINITY;
-                    l_run[ob] = 0.f;
-                }
-                bool aborted = false;
-
-                int64_t rows[NI];
-                int32_t pg_next;
-                u32x4_t kr[NI], vr[NI];
-                const int64_t lane_off = head_off + (lval ? wbase + 8 * sl : 0);
-                auto issue = [&](const uint16_t* base, u32x4_t (&dst)[NI]) {
-#pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        dst[i] = ldg16_stream(base + rows[i] + lane_off);
-                };
-
-                // One 32-key tile per step.  At the top of step t the registers holding the
-                // K/V of tile t are written to LDS and at once refilled with tile t+1, which
-                // so has a whole step to arrive.  Every request is unconditional (a tile
-                // past the segment reads the safe row, page entries are read at clamped
-                // indices): the loop has no divergent branches and each wait on the memory
-                // counter is exact.  The issue order (page entries, V, K) is pinned with
-                // scheduling barriers, here and in the loop: the compiler's waits at the
-                // loop head are exact only if both paths into it issue in the same order.
-                tile_rows(t0, tile_page(t0), rows);
-                pg_next = tile_page(t0 + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                issue(a.k_pages, kr);
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (MODE != kMaxScan)
-                    issue(a.v_pages, vr);
-                __builtin_amdgcn_sched_barrier(0);
-                // An abandoned lazy segment leaves by the loop condition only: an exit between
-                // the softmax and the PV product would make the compiler keep a second copy of
-                // every accumulator.  The tile that triggered it still runs its (discarded) PV.
-                for (int32_t t = t0; t < t1 && !aborted; ++t) {
-                    const int32_t k0 = g.kv_lo + t * kTK;
-                    // (1) this wave's K and V slices -> LDS [key][d_local].  Keys past the
-                    // request hold the safe row and d past head_dim the row start: finite
-                    // values whose weight (masked logit) or output column (never stored) is 0.
-                    if constexpr (MODE != kMaxScan) {
-#pragma unroll
-                        for (int i = 0; i < NI; ++i)
-                            *reinterpret_cast<u32x4_t*>(vls + C::vofs(i * KPI + kl, 2 * sl)) = vr[i];
-                    }
-#pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        *reinterpret_cast<u32x4_t*>(kls + C::kofs(i * KPI + kl, sl)) = kr[i];
-                    // request tile t+1 (page entries of t+2 first, so that waiting for them
-                    // later never waits for K/V)
-                    tile_rows(t + 1, pg_next, rows);
-                    pg_next = tile_page(t + 2);
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue(a.k_pages, kr);
-                    __builtin_amdgcn_sched_barrier(0);
-                    // (2) partial S^T over this wave's d-slice (absent d: Q is zero there and K
-                    //     finite; absent keys are masked below).  A operand: key 16h + l16,
-                    //     d chunk 4s + grp4 of the slice.
-                    bf16x8_t kb[2][KS];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int s = 0; s < KS; ++s)
-                            kb[h][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kls + C::kofs(16 * h + l16, 4 * s + grp4)));
-#pragma unroll
-                    for (int b = 0; b < RT; ++b) {
-                        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int s = 0; s < KS; ++s) {
-                            acc0 = mfma16(kb[0][s], qf[b][s], acc0);
-                            acc1 = mfma16(kb[1][s], qf[b][s], acc1);
-                        }
-                        sx[((wave * 2 + 0) * RT + b) * 64 + lane] = acc0;
-                        sx[((wave * 2 + 1) * RT + b) * 64 + lane] = acc1;
-                    }
-                    __syncthreads();
-                    // V of tile t+1: requested here rather than with K so that the two
-                    // halves of the workgroup's 64 KB do not queue at the address unit at once
-                    if constexpr (MODE != kMaxScan)
-                        issue(a.v_pages, vr);
-                    __builtin_amdgcn_sched_barrier(0);
-                    // (3) owners: reduce, mask, softmax, publish P^T
-#pragma unroll
-                    for (int ob = 0; ob < NOWN; ++ob) {
-                        const int b = ob * WAVES + wave;
-                        if (b < RT) {
-                            // partials are requested four at a time before any is summed, so that
-                            // the LDS latency is paid once per four
-                            float z[8];
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                                for (int w0 = 0; w0 < WAVES; w0 += 4) {
-                                    f32x4_t part[4];
-#pragma unroll
-                                    for (int ww = 0; ww < 4; ++ww)
-                                        part[ww] = sx[(((w0 + ww) * 2 + h) * RT + b) * 64 + lane];
-                                    acc += (part[0] + part[1]) + (part[2] + part[3]);
-                                }
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    z[h * 4 + e] = acc[e];
-                            }
-                            float tmax = -INFINITY;
-                            if (k0 >= ilo[ob] && k0 + kTK - 1 <= ihi[ob]) {
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) {
-                                    z[e] *= a.scale_log2;
-                                    tmax = fmaxf(tmax, z[e]);
-                                }
-                            } else {
-                                const int32_t lo = rlo[ob], hi = rhi[ob];
-#pragma unroll
-                                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                                    for (int e = 0; e < 4; ++e) {
-                                        const int32_t key = k0 + 16 * h + 4 * grp4 + e;
-                                        const bool vis = key >= lo && key <= hi;
-                                        const float zz = vis ? z[h * 4 + e] * a.scale_log2 : -INFINITY;
-                                        z[h * 4 + e] = zz;
-                                        tmax = fmaxf(tmax, zz);
-                                    }
-                            }
-                            tmax = max_across_groups(tmax);
-                            if constexpr (MODE == kMaxScan) {
-                                m_fix[ob] = fmaxf(m_fix[ob], tmax);
-                            } else {
-                                const float m_old = m_run[ob];
-                                float m_new = m_old;
-                                bool over = false;
-                                if constexpr (MODE == kLazy) {
-                                    const bool first = m_old == -INFINITY;
-                                    over = !first && tmax > m_old + kLazyBound;
-                                    m_new = first ? tmax : m_old;
-                                }
-                                const float mu = (m_new == -INFINITY) ? 0.f : m_new;
-                                u32x4_t pk;
-                                // the denominator sums the same bf16-rounded weights PV uses
-                                // (a dot product of each packed pair with (1, 1))
-                                const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-                                float psum = l_run[ob];
-#pragma unroll
-                                for (int e2 = 0; e2 < 4; ++e2) {
-                                    const uint32_t w2 = pack_bf16x2(__builtin_amdgcn_exp2f(z[2 * e2] - mu),
-                                                                    __builtin_amdgcn_exp2f(z[2 * e2 + 1] - mu));
-                                    pk[e2] = w2;
-                                    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2), ones, psum,
-                                                                          false);
-                                }
-                                l_run[ob] = psum;
-                                m_run[ob] = m_new;
-                                px[b * 64 + lane] = pk;
-                                if constexpr (MODE == kLazy) {
-                                    const unsigned long long anyover = __ballot(over);
-                                    if (lane == 0)
-                                        flag_s[b] = anyover ? 1 : 0;
-                                }
-                            }
-                        }
-                    }
-                    __syncthreads();
-                    if constexpr (MODE == kMaxScan)
-                        continue;
-                    if constexpr (MODE == kLazy) {
-                        int anyover = 0;
-#pragma unroll
-                        for (int b = 0; b < RT; ++b)
-                            anyover |= flag_s[b];
-                        aborted = __builtin_amdgcn_readfirstlane(anyover) != 0;
-                    }
-                    // (4) O^T += V^T P^T for this wave's d-slice
-                    // A operand V^T: lane l holds d = 16c + l%16 at key slots 4*grp4 + 0..3
-                    // and 16 + 4*grp4 + 0..3 (the key order of P^T).  Transposing reads:
-                    // lane j of group grp4 addresses key 4*grp4 + j/4 (and +16) at
-                    // d = 16c + 4*(j%4).  All reads are issued before the first product.
-                    bf16x8_t pb[RT];
-#pragma unroll
-                    for (int b = 0; b < RT; ++b)
-                        pb[b] = as_bf16x8(px[b * 64 + lane]);
-                    const int vrow = 4 * grp4 + (l16 >> 2);
-                    u32x2_t vt[DT][2];
-#pragma unroll
-                    for (int c = 0; c < DT; ++c) {
-                        vt[c][0] = ds_read_tr16(vls + C::vofs(vrow, 4 * c + (l16 & 3)));
-                        vt[c][1] = ds_read_tr16(vls + C::vofs(vrow + 16, 4 * c + (l16 & 3)));
-                    }
-#pragma unroll
-                    for (int c = 0; c < DT; ++c) {
-                        const u32x4_t va = {vt[c][0][0], vt[c][0][1], vt[c][1][0], vt[c][1][1]};
-                        const bf16x8_t vb = as_bf16x8(va);
-#pragma unroll
-                        for (int b = 0; b < RT; ++b)
-                            o[c][b] = mfma16(vb, pb[b], o[c][b]);
-                    }
-                }
-                // wait for the last tile's LDS traffic of every wave before anything reuses it
-                __syncthreads();
-                return aborted;
-            };
-
-            if constexpr (PHASE == 0) {
-                if (run_pass(std::integral_constant<int, kLazy>{})) {
-                    if (this_seg < 64)
-                        redo_mask |= (uint64_t)1 << this_seg;
-                    else
-                        redo_overflow = true;
-                    continue;  // recomputed after the run
-                }
-            } else {
-                run_pass(std::integral_constant<int, kMaxScan>{});
-                run_pass(std::integral_constant<int, kFixed>{});
-            }
-
-            // ---------------- epilogue ----------------
-#pragma unroll
-            for (int ob = 0; ob < NOWN; ++ob) {
-                const int b = ob * WAVES + wave;
-                if (b < RT) {
-                    float l = l_run[ob];
-                    l += __shfl_xor(l, 16);
-                    l += __shfl_xor(l, 32);
-                    if (grp4 == 0) {
-                        lsum_s[b * 16 + l16] = l;
-                        mref_s[b * 16 + l16] = m_run[ob];
-                    }
-                }
-            }
-            __syncthreads();
-            const int64_t sbase = ((int64_t)wg * 2 + slot) * d.rmax;
-#pragma unroll
-            for (int b = 0; b < RT; ++b) {
-                const int32_t row = b * 16 + l16;
-                if (row < rows_here) {
-                    const float l = lsum_s[row];
-                    const float inv = l > 0.f ? 1.f / l : 0.f;
-                    const int32_t rr = row0 + row;
-                    const int32_t qi = rr / G;
-                    const int32_t qj = rr % G;
-                    uint16_t* orow = a.out + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
-                    float* prow = a.part_o + (sbase + row) * a.Dp;
-#pragma unroll
-                    for (int c = 0; c < DT; ++c) {
-                        const int32_t dd = wbase + 16 * c + 4 * grp4;
-                        if (dd < D) {
-                            const f32x4_t v = o[c][b] * inv;
-                            if (whole) {
-                                const u32x2_t pk2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                                *reinterpret_cast<u32x2_t*>(orow + dd) = pk2;
-                            } else {
-                                *reinterpret_cast<f32x4_t*>(prow + dd) = v;
-                            }
-                        }
-                    }
-                    if (!whole && wave == 0 && grp4 == 0)
-                        a.part_lse[sbase + row] = l > 0.f ? mref_s[row] + log2f(l) : -INFINITY;
-                }
-            }
-            __syncthreads();
-        }
-    };
-
-    walk(std::integral_constant<int, 0>{});
-    if (redo_mask != 0 || redo_overflow)
-        walk(std::integral_constant<int, 1>{});
-}
-
-// Raises a kernel's dynamic-LDS limit once per device (not on every launch: a call
-// being captured into a graph then enqueues nothing but the launch itself).
-template <int DP, int RT, bool EXACT>
-static hipError_t ensure_lds_limit()
-{
-    using C = Cfg<DP, RT>;
-    if (C::LDS_BYTES <= 64 * 1024)
-        return hipSuccess;
-    static std::atomic<uint64_t> done{0};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return e;
-    const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
-    if (bit && (done.load(std::memory_order_acquire) & bit))
-        return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel<DP, RT, EXACT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e == hipSuccess && bit)
-        done.fetch_or(bit, std::memory_order_release);
-    return e;
-}
-
-template <int DP, int RT, bool EXACT>
-static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
-{
-    using C = Cfg<DP, RT>;
-    const hipError_t e = ensure_lds_limit<DP, RT, EXACT>();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((attn_mfma_kernel<DP, RT, EXACT>), dim3(a.d.P), dim3(C::THREADS), C::LDS_BYTES, stream, a);
-    return hipGetLastError();
-}
-
-template <int DP, bool EXACT>
-static hipError_t launch_rt(const AttnArgs& a, int row_tiles, hipStream_t stream)
-{
-    switch (row_tiles) {
-    case 1: return launch_one<DP, 1, EXACT>(a, stream);
-    case 2: return launch_one<DP, 2, EXACT>(a, stream);
-    case 3: return launch_one<DP, 3, EXACT>(a, stream);
-    case 4: return launch_one<DP, 4, EXACT>(a, stream);
-    case 5: return launch_one<DP, 5, EXACT>(a, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <int DP>
-static hipError_t launch_dp(const AttnArgs& a, int row_tiles, hipStream_t stream)
-{
-    return a.D == DP ? launch_rt<DP, true>(a, row_tiles, stream) : launch_rt<DP, false>(a, row_tiles, stream);
-}
-
 hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream)
 {
-    switch (dpad) {
-    case 128: return launch_dp<128>(a, row_tiles, stream);
-    case 256: return launch_dp<256>(a, row_tiles, stream);
-    case 512: return launch_dp<512>(a, row_tiles, stream);
-    default: return hipErrorInvalidValue;
-    }
+    if (a.span_offsets)
+        return launch_attn_mfma_spans(a, dpad, row_tiles, stream);
+    return launch_dp<false>(a, dpad, row_tiles, stream);
 }
 
 // Resident workgroups per CU, queried once per kernel instance (the library runs on
-// one architecture, so the answer does not depend on the device).
+// one architecture, so the answer does not depend on the device).  The span
+// instances differ only in a few set-up instructions and share the plain ones'
+// launch shape; the planner's count is an upper bound on workgroups in flight,
+// not something the kernel relies on.
 template <int DP, int RT, bool EXACT>
 static int occupancy_one()
 {
@@ -716,9 +24,9 @@ static int occupancy_one()
     int blocks = cached.load(std::memory_order_acquire);
     if (blocks >= 0)
         return blocks;
-    if (ensure_lds_limit<DP, RT, EXACT>() != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT>, Cfg<DP, RT>::THREADS,
-                                                     Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
+    if (ensure_lds_limit<DP, RT, EXACT, false>() != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT, false>,
+                                                     Cfg<DP, RT>::THREADS, Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
         return 0;
     cached.store(blocks, std::memory_order_release);
     return blocks;

@@ -141,6 +141,8 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
                     const int32_t i = (row0 + rho) / G;
                     int32_t lo, hi;
                     query_range(L, n, i, is_causal, d.window, lo, hi);
+                    if (is_causal && a.span_offsets)
+                        hi = span_high(a.span_offsets, a.spans, a.num_spans, r, L + i, L + n, hi);
                     if (key >= lo && key <= hi) {
                         float s = 0.f;
                         for (int32_t dd = 0; dd < D; ++dd)

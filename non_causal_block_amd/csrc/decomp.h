@@ -99,4 +99,27 @@ DFL_HD void query_range(int32_t L, int32_t n, int32_t i, bool causal, int32_t wi
     }
 }
 
+// High end of a causal row's range once bidirectional spans are applied: a
+// query at position p inside a span [s, e) also sees the span's later keys
+// (the mm-prefix case -- a multimodal prefix is attended as a whole while
+// text stays causal; kenforever1 "DFlash + Gemma 4 31B-it" notes, section on
+// MooreThreads/vllm-musa PR #52).  The request's spans are entries
+// offs[r] .. offs[r+1]-1 of `spans` ((start, end) pairs); entries outside
+// [0, num_spans) are ignored, and the result never passes T - 1.  Any order
+// and any overlap give the same answer: the largest end among the spans that
+// hold p.
+DFL_HD int32_t span_high(const int32_t* offs, const int32_t* spans, int32_t num_spans, int32_t r, int32_t p,
+                         int32_t T, int32_t hi)
+{
+    int32_t w0 = offs[r], w1 = offs[r + 1];
+    w0 = w0 < 0 ? 0 : w0;
+    w1 = w1 > num_spans ? num_spans : w1;
+    for (int32_t w = w0; w < w1; ++w) {
+        const int32_t s = spans[2 * w], e = spans[2 * w + 1];
+        if (s <= p && p < e && e - 1 > hi)
+            hi = e - 1;
+    }
+    return hi < T - 1 ? hi : T - 1;
+}
+
 }  // namespace dflash

@@ -156,6 +156,9 @@ struct AttnArgs {
     const int32_t* ctx_lens;
     const int32_t* block_lens;
     const uint8_t* causal;
+    const int32_t* span_offsets;  // [B+1] or nullptr: bidirectional spans of causal requests
+    const int32_t* spans;         // [num_spans][2] (start, end) key positions
+    int32_t num_spans;
     uint16_t* out;
     float* part_o;     // [P][2][rmax][Dp]
     float* part_lse;   // [P][2][rmax]

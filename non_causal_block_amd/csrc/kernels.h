@@ -16,6 +16,8 @@ int ref_wgs_per_cu();  // resident workgroups per CU on the current device (0 if
 // MFMA kernel.  `row_tiles` is the number of 16-row MFMA tiles per unit
 // (rows per unit = 16 * row_tiles); `dpad` is 128, 256 or 512.
 hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
+// the same with bidirectional spans (a.span_offsets non-null); attn_mfma_spans.hip
+hipError_t launch_attn_mfma_spans(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
 int mfma_tile_keys();
 int mfma_max_row_tiles(int dpad);
 int mfma_wgs_per_cu(int dpad, int row_tiles, bool exact);  // on the current device (0 if unknown)

@@ -36,12 +36,21 @@ def upload(wl: workloads.Workload) -> dict:
 
 
 def run(wl: workloads.Workload, t: dict = None, *, kernel=nb.DFLASH_KERNEL_AUTO, num_workgroups=0,
-        hints=True, causal_none=False, out=None) -> torch.Tensor:
+        hints=True, causal_none=False, out=None, spans=None) -> torch.Tensor:
+    """``spans``: per-request (start, end) lists -> dflash_block_attn_spans."""
     t = t or upload(wl)
+    so = sp = None
+    if spans is not None:
+        offs = np.zeros(wl.B + 1, dtype=np.int32)
+        offs[1:] = np.cumsum([len(x) for x in spans])
+        flat = np.asarray([p for x in spans for p in x], dtype=np.int32).reshape(-1, 2)
+        so = torch.from_numpy(offs).to(dev())
+        sp = torch.from_numpy(np.ascontiguousarray(flat)).to(dev()) if flat.shape[0] else None
     o = nb.block_attn(t["q"], t["k"], t["v"], t["pt"], t["ctx"], t["blk"],
                       causal=None if causal_none else t["causal"], window=wl.window, scale=wl.scale, out=out,
                       max_block_len=int(wl.block_lens.max()) if (hints and wl.B) else 0,
-                      total_kv_len=wl.total_kv if hints else 0, kernel=kernel, num_workgroups=num_workgroups)
+                      total_kv_len=wl.total_kv if hints else 0, kernel=kernel, num_workgroups=num_workgroups,
+                      span_offsets=so, spans=sp)
     torch.cuda.synchronize()
     return o
 

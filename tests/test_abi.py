@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -150,6 +150,25 @@ def test_rejects_before_launch(lib):
     d.workspace = FAKE + 16
     d.workspace_bytes = need
     expect(call(d), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+
+
+def test_spans_call_rejects_before_launch(lib):
+    d = desc()
+
+    def sp(offs=FAKE, spans=FAKE, num=3, dd=d, q=FAKE):
+        return nb.dflash_block_attn_spans(q, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 4, 512, FAKE, offs, spans, num, 0,
+                                          0.044, FAKE, None, dd)
+
+    expect(sp(num=-1), nb.DFLASH_ERR_INVALID_ARGUMENT, "num_spans")
+    expect(sp(spans=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "spans is NULL")
+    expect(sp(offs=FAKE + 2), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    expect(sp(spans=FAKE + 1), nb.DFLASH_ERR_INVALID_ARGUMENT, "aligned")
+    expect(sp(q=0), nb.DFLASH_ERR_INVALID_ARGUMENT, "NULL")
+    # the span checks pass with no spans at all or without span_offsets; then the
+    # missing workspace is what fails
+    expect(sp(spans=0, num=0), nb.DFLASH_ERR_WORKSPACE_TOO_SMALL, "needs")
+    expect(sp(offs=0, spans=0, num=-1), nb.DFLASH_ERR_WORKSPACE_TOO_SMALL, "needs")
+    expect(sp(dd=desc(total_q=0)), nb.DFLASH_OK)
 
 
 @pytest.mark.parametrize("field,value", [

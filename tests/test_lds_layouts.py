@@ -1,4 +1,4 @@
-"""CPU model of the MFMA kernel's LDS tile layouts (attn_mfma.hip).
+"""CPU model of the MFMA kernel's LDS tile layouts (attn_mfma_kernel.h).
 
 The kernel stages each wave's K and V d-slices of a 32-key tile in LDS.  This
 test restates the index arithmetic of the stores and the reads (the formulas

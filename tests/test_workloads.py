@@ -73,3 +73,20 @@ def test_values_are_standard_normal():
     wl = workloads.make("c3_global_d512", ctx_cap=2000, B=2)
     x = workloads.bf16_bits_to_f32(wl.k).astype(np.float64)
     assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+
+
+def test_draw_spans_are_sorted_disjoint_and_inside_the_request():
+    ctx = np.array([0, 5, 100, 20000, 3, 0], dtype=np.int32)
+    blk = np.array([16, 9, 0, 9, 1, 0], dtype=np.int32)
+    hits = 0
+    for seed in range(40):
+        spans = workloads.draw_spans(ctx, blk, seed=seed)
+        assert spans == workloads.draw_spans(ctx, blk, seed=seed)
+        assert len(spans) == len(ctx)
+        for L, n, lst in zip(ctx.tolist(), blk.tolist(), spans):
+            end = 0
+            for s, e in lst:
+                assert end <= s < e <= L + n
+                end = e
+                hits += e > L and n > 0
+    assert hits > 20   # spans reach into blocks often enough to matter

@@ -269,6 +269,39 @@ def block_conv_inputs(block_lens, channels: int, groups: int, taps: int, seed: i
     return x, base, delta
 
 
+def draw_spans(ctx_lens, block_lens, seed: int, max_prefix_span: int = 512):
+    """Seeded bidirectional spans (the multimodal-prefix mask), one list per request.
+
+    Each request gets, each with probability 1/2, in position order and disjoint:
+    an image span inside the context (length U[1, max_prefix_span]); a span that
+    starts within 16 positions before the block (or at its start) and ends
+    U-uniformly inside the block or at its end; and one more span inside the
+    rest of the block.  Only spans that hold block positions change a block
+    query's mask; the context-only span is there to exercise the lookup.  The
+    mix is a reading: the pages name the mask, not a span-length law.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for L, n in zip(np.asarray(ctx_lens).tolist(), np.asarray(block_lens).tolist()):
+        T, lst, pos = L + n, [], 0
+        if L > 0 and rng.random() < 0.5:
+            s = int(rng.integers(0, L))
+            e = min(L, s + int(rng.integers(1, max_prefix_span + 1)))
+            lst.append((s, e))
+            pos = e
+        if n > 0 and rng.random() < 0.5:
+            s = int(rng.integers(max(pos, L - 16), L + 1))
+            e = int(rng.integers(max(s, L) + 1, T + 1))
+            lst.append((s, e))
+            pos = e
+        if pos < T and max(pos, L) < T and rng.random() < 0.5:
+            s = int(rng.integers(max(pos, L), T))
+            e = int(rng.integers(s + 1, T + 1))
+            lst.append((s, e))
+        out.append(lst)
+    return out
+
+
 def split_block_kv(wl: "Workload"):
     """The block tokens' K/V rows and pages that hold only the context.
 
