@@ -143,7 +143,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str) -> dict:
     attn_name, attn_fetch = pick(fetch, "attn_mfma_kernel")
     _, attn_write = pick(write, "attn_mfma_kernel")
     _, read_cal = pick(fetch, "stream_read_kernel")
-    _, write_cal = pick(write, "FillFunctor")
+    _, write_cal = pick(write, "FillFunctor<float>")  # the flush buffer (float); other fills are tiny
     f_read = FLUSH_BYTES / (read_cal * 1024.0)
     f_write = FLUSH_BYTES / (write_cal * 1024.0)
     fetch_b = attn_fetch * 1024.0 * f_read
