@@ -74,6 +74,13 @@ int device_cus(int* out)
 // runs of one or two tiles (and a combine over more pieces) finish soonest;
 // large steps fill the chip long before this bound matters.
 constexpr int kMinTilesPerWg = 2;
+// Set-up charge of a unit in the work split (decomp.h), in tiles: what one more
+// unit in a run costs the MFMA kernel (queries and first pages in, output or
+// partial out -- about 3.5 tiles' time at head_dim 512 and 80 rows, measured).
+// Applied only when runs are long (at least kChargeMinTiles tiles): short runs
+// are latency-bound and want the plain equal split.
+constexpr int kSegmentCharge = 3;
+constexpr int kChargeMinTiles = 16;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -86,6 +93,7 @@ struct Plan {
     int row_tiles = 0;
     int Dp = 0;
     int combine_wgs = 0;
+    int ov = 0;
     size_t off_lse = 0;
     size_t ws_bytes = 0;
     bool empty = false;
@@ -181,6 +189,14 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
     if (P > (1 << 20))
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_workgroups %lld too large", (long long)P);
     p->P = (int)P;
+    if (kernel == DFLASH_KERNEL_MFMA && desc->total_kv_len > 0) {
+        int64_t groups = 1;
+        if (desc->max_block_len > 0)
+            groups = ((int64_t)desc->max_block_len * G + p->rmax - 1) / p->rmax;
+        const int64_t tiles = (int64_t)Hkv * groups * (desc->total_kv_len / p->tk);
+        if (tiles >= (int64_t)kChargeMinTiles * P)
+            p->ov = kSegmentCharge;
+    }
     if (p->P > 1) {
         const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(float);
         p->off_lse = align_up(o_bytes);
@@ -256,6 +272,7 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.d.rmax = p.rmax;
     a.d.tk = p.tk;
     a.d.P = p.P;
+    a.d.ov = p.ov;
     a.Hq = n_heads;
     a.D = head_dim;
     a.Dp = p.Dp;

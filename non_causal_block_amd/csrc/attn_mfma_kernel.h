@@ -259,15 +259,16 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 ++r;
                 continue;
             }
-            const int64_t off = pos - rbase;
-            const int32_t unit = (int32_t)(off / g.ntiles);
+            const Segment sg = run_segment(g, rbase, pos, end, d.ov);
+            pos = sg.next;
+            if (sg.t0 >= sg.t1)
+                continue;  // only set-up positions of this unit: nothing to do here
+            const int32_t unit = sg.unit;
             // segment bounds are wave-uniform; readfirstlane lets the compiler keep the tile
             // loop in scalar control flow with exact memory-counter waits
-            const int32_t t0 = __builtin_amdgcn_readfirstlane((int32_t)(off % g.ntiles));
-            const int64_t seg_end = min(end, rbase + (int64_t)(unit + 1) * g.ntiles);
-            const int32_t t1 = __builtin_amdgcn_readfirstlane((int32_t)(seg_end - rbase - (int64_t)unit * g.ntiles));
+            const int32_t t0 = __builtin_amdgcn_readfirstlane(sg.t0);
+            const int32_t t1 = __builtin_amdgcn_readfirstlane(sg.t1);
             const int this_seg = seg++;
-            pos = seg_end;
             if constexpr (PHASE == 1) {
                 const bool redo = this_seg < 64 ? ((redo_mask >> this_seg) & 1u) != 0 : redo_overflow;
                 if (!redo)

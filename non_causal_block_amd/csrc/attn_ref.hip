@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
         qstart += a.block_lens[i];
 
     int64_t pos = begin;
+    int nseg = 0;
     while (pos < end) {
         const int32_t L = a.ctx_lens[r];
         const int32_t n = a.block_lens[r];
@@ -67,14 +68,16 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
             ++r;
             continue;
         }
-        const int64_t off = pos - rbase;
-        const int32_t unit = (int32_t)(off / g.ntiles);
-        const int32_t t0 = (int32_t)(off % g.ntiles);
-        const int64_t seg_end = min(end, rbase + (int64_t)(unit + 1) * g.ntiles);
-        const int32_t t1 = (int32_t)(seg_end - rbase - (int64_t)unit * g.ntiles);
+        const Segment sg = run_segment(g, rbase, pos, end, d.ov);
+        pos = sg.next;
+        if (sg.t0 >= sg.t1)
+            continue;  // only set-up positions of this unit
+        const int32_t unit = sg.unit;
+        const int32_t t0 = sg.t0;
+        const int32_t t1 = sg.t1;
         const int32_t kvh = unit / g.ngroups;
         const int32_t grp = unit % g.ngroups;
-        const int slot = (pos == begin) ? 0 : 1;
+        const int slot = (nseg++ == 0) ? 0 : 1;  // first unit with real tiles in the run: slot 0
         const bool whole = (t0 == 0 && t1 == g.ntiles);
         const bool is_causal = a.causal ? (a.causal[r] != 0) : false;
         const int32_t row0 = grp * d.rmax;
@@ -213,7 +216,6 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
                 a.part_lse[sbase + rho] = l > 0.f ? m_s[rho] + log2f(l) : -INFINITY;
         }
         __syncthreads();
-        pos = seg_end;
     }
 }
 

@@ -48,10 +48,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int32_t grp = rowreq / d.rmax;
     const int32_t rin = rowreq % d.rmax;
     const int32_t unit = kvh * g.ngroups + grp;
-    const int64_t us = rbase + (int64_t)unit * g.ntiles;
-    const int64_t ue = us + g.ntiles;
-    const int64_t kf = us / tpw;
-    const int64_t kl = (ue - 1) / tpw;
+    const int64_t us = rbase + (int64_t)unit * g.uwork;
+    int64_t kf, kl;
+    unit_pieces(g, us, d.ov, tpw, kf, kl);
     if (kf == kl)
         return;  // finished inside one workgroup, already written
 
@@ -61,7 +60,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     for (int64_t base = 0; base < npieces; base += 64) {
         const int64_t k = kf + base + lane;
         if (k <= kl) {
-            const int slot = (k == kf && us != k * tpw) ? 1 : 0;
+            const int slot = piece_slot(k, us, tpw);
             M = fmaxf(M, a.part_lse[(k * 2 + slot) * d.rmax + rin]);
         }
     }
@@ -80,7 +79,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
         const int64_t kq = kf + base + lane;
         float wl = 0.f;
         if (kq <= kl) {
-            const int slot = (kq == kf && us != kq * tpw) ? 1 : 0;
+            const int slot = piece_slot(kq, us, tpw);
             const float lse = a.part_lse[(kq * 2 + slot) * d.rmax + rin];
             wl = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
         }
@@ -95,7 +94,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
                 const int j = min(j0 + u, cnt - 1);
                 wj[u] = (j0 + u < cnt) ? __shfl(wl, j) : 0.f;
                 const int64_t k = kf + base + j;
-                const int slot = (k == kf && us != k * tpw) ? 1 : 0;
+                const int slot = piece_slot(k, us, tpw);
                 const int64_t prow = (k * 2 + slot) * d.rmax + rin;
                 if (dlive && wj[u] != 0.f) {
                     const float4* src = reinterpret_cast<const float4*>(a.part_o + prow * a.Dp + d0);

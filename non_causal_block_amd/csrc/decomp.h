@@ -17,10 +17,20 @@
 // range is cut into ceil((T - lo)/tk) tiles.  Units are laid out request by
 // request, kv-head-major inside a request, and every workgroup w of the P
 // attention workgroups takes the tiles [w*tpw, (w+1)*tpw) of that flat order,
-// tpw = ceil(total/P).  A unit whose tiles all fall to one workgroup is
-// finished there; otherwise every workgroup that touched it leaves a partial
-// (normalised output + log2-sum-exp) in one of its two slots:
-//     slot 0 -- the unit was the first one in the workgroup's run,
+// tpw = ceil(total/P).
+//
+// Set-up charge.  Starting a unit costs a workgroup more than a tile: loading
+// the unit's queries and first pages, and writing its output or partial at
+// the end.  A run that crosses from one unit into the next pays that twice, so
+// the flat order gives every unit `ov` virtual tiles in front of its real
+// ones: a unit spans uwork = ov + ntiles flat positions, virtual position v
+// being real tile v - ov (none for v < ov).  A run whose part of a unit holds
+// only virtual positions does nothing there.  ov = 0 is the plain split.
+//
+// A unit whose real tiles all fall to one workgroup is finished there;
+// otherwise every workgroup that holds some of its real tiles leaves a
+// partial (normalised output + log2-sum-exp) in one of its two slots:
+//     slot 0 -- the unit was the first one with real tiles in the run,
 //     slot 1 -- the unit was the last one (and not also the first).
 // Units strictly inside a run are always whole.
 #pragma once
@@ -43,12 +53,14 @@ struct Decomp {
     int32_t rmax;    // rows per unit (row group size)
     int32_t tk;      // keys per tile
     int32_t P;       // attention workgroups
+    int32_t ov;      // virtual set-up tiles charged at the start of every unit
 };
 
 struct ReqGeom {
     int32_t kv_lo;    // first key of tile 0 (multiple of tk)
     int32_t T;        // keys of the request (L + n)
-    int32_t ntiles;   // tiles per unit
+    int32_t ntiles;   // real tiles per unit
+    int32_t uwork;    // flat positions per unit: ov + ntiles (0 without queries)
     int32_t ngroups;  // row groups per kv-head
 };
 
@@ -59,6 +71,7 @@ DFL_HD ReqGeom req_geom(int32_t L, int32_t n, const Decomp& d)
     if (n <= 0) {
         g.kv_lo = 0;
         g.ntiles = 0;
+        g.uwork = 0;
         g.ngroups = 0;
         return g;
     }
@@ -71,14 +84,55 @@ DFL_HD ReqGeom req_geom(int32_t L, int32_t n, const Decomp& d)
     lo = (lo / d.tk) * d.tk;
     g.kv_lo = lo;
     g.ntiles = (g.T - lo + d.tk - 1) / d.tk;
+    g.uwork = d.ov + g.ntiles;
     g.ngroups = (n * d.G + d.rmax - 1) / d.rmax;
     return g;
 }
 
-// Tiles of all units of one request.
+// Flat positions of all units of one request.
 DFL_HD int64_t req_work(const ReqGeom& g, const Decomp& d)
 {
-    return (int64_t)d.Hkv * g.ngroups * g.ntiles;
+    return (int64_t)d.Hkv * g.ngroups * g.uwork;
+}
+
+// The part of one unit that a run [pos, end) covers, for pos inside a request
+// whose flat range starts at rbase: unit index, real tiles [t0, t1) (empty
+// when the part holds only virtual positions) and the flat position after it.
+struct Segment {
+    int32_t unit;
+    int32_t t0;
+    int32_t t1;
+    int64_t next;
+};
+
+DFL_HD Segment run_segment(const ReqGeom& g, int64_t rbase, int64_t pos, int64_t end, int32_t ov)
+{
+    Segment s;
+    s.unit = (int32_t)((pos - rbase) / g.uwork);
+    const int64_t ustart = rbase + (int64_t)s.unit * g.uwork;
+    const int64_t uend = ustart + g.uwork;
+    s.next = end < uend ? end : uend;
+    const int64_t v0 = pos - ustart - ov;
+    const int64_t v1 = s.next - ustart - ov;
+    s.t0 = (int32_t)(v0 > 0 ? v0 : 0);
+    s.t1 = (int32_t)(v1 > 0 ? v1 : 0);
+    return s;
+}
+
+// Workgroups [kf, kl] hold real tiles of the unit whose flat range starts at
+// `us`; kf == kl means one workgroup finished it whole.
+DFL_HD void unit_pieces(const ReqGeom& g, int64_t us, int32_t ov, int64_t tpw, int64_t& kf, int64_t& kl)
+{
+    kf = (us + ov) / tpw;
+    kl = (us + g.uwork - 1) / tpw;
+}
+
+// Slot holding workgroup k's partial of the unit starting at `us`: 1 when the
+// run began before the unit (it then holds real tiles of an earlier unit --
+// every unit ends with a real tile), else 0.
+DFL_HD int piece_slot(int64_t k, int64_t us, int64_t tpw)
+{
+    return k * tpw < us ? 1 : 0;
 }
 
 DFL_HD int64_t tiles_per_wg(int64_t total, int32_t P)

@@ -1,8 +1,9 @@
 // Host check of the work split in decomp.h (compiled with g++ by tests/test_decomp.py).
 //
-// Reads a case from stdin:  B Hkv G window rmax tk P  then B lines "L n".
+// Reads a case from stdin:  B Hkv G window rmax tk P ov  then B lines "L n".
 // Walks every workgroup's run exactly as the kernels do and checks that
-//   * every tile of every unit is processed by exactly one workgroup,
+//   * every real tile of every unit is processed by exactly one workgroup,
+//   * a run's part of a unit that holds only set-up positions does nothing,
 //   * a unit handled whole by one workgroup is not also split,
 //   * the pieces of a split unit are exactly the (workgroup, slot) pairs the
 //     combine kernel derives from the unit's own tile range,
@@ -22,13 +23,15 @@ using namespace dflash;
 int main()
 {
     Decomp d;
-    if (scanf("%d %d %d %d %d %d %d", &d.B, &d.Hkv, &d.G, &d.window, &d.rmax, &d.tk, &d.P) != 7)
+    if (scanf("%d %d %d %d %d %d %d %d", &d.B, &d.Hkv, &d.G, &d.window, &d.rmax, &d.tk, &d.P, &d.ov) != 8)
         return 2;
     std::vector<int> L(d.B), n(d.B);
     for (int r = 0; r < d.B; ++r)
         if (scanf("%d %d", &L[r], &n[r]) != 2)
             return 2;
     int64_t total = 0;
+    if (d.ov < 0)
+        return 2;
     std::vector<int64_t> rbase(d.B + 1, 0);
     for (int r = 0; r < d.B; ++r) {
         ReqGeom g = req_geom(L[r], n[r], d);
@@ -39,7 +42,8 @@ int main()
 
     // unit key -> list of (wg, slot, whole)
     std::map<std::tuple<int, int, int>, std::vector<std::tuple<int64_t, int, bool>>> pieces;
-    std::vector<int> tile_hits(total, 0);
+    // (request, unit, real tile) -> times processed
+    std::map<std::tuple<int, int, int>, int> tile_hits;
     std::set<std::pair<int64_t, int>> slots_used;
     for (int64_t wg = 0; wg < d.P; ++wg) {
         const int64_t begin = wg * tpw;
@@ -60,16 +64,19 @@ int main()
                 ++r;
                 continue;
             }
-            const int64_t off = pos - rb;
-            const int unit = (int)(off / g.ntiles);
-            const int t0 = (int)(off % g.ntiles);
-            const int64_t seg_end = std::min<int64_t>(end, rb + (int64_t)(unit + 1) * g.ntiles);
-            const int t1 = (int)(seg_end - rb - (int64_t)unit * g.ntiles);
-            const bool whole = t0 == 0 && t1 == g.ntiles;
+            const Segment sg = run_segment(g, rb, pos, end, d.ov);
+            if (sg.next <= pos || sg.t1 > g.ntiles || sg.t0 < 0) {
+                printf("FAIL segment bounds\n");
+                return 1;
+            }
+            pos = sg.next;
+            if (sg.t0 >= sg.t1)
+                continue;
+            const bool whole = sg.t0 == 0 && sg.t1 == g.ntiles;
             const int slot = seg == 0 ? 0 : 1;
-            for (int64_t t = pos; t < seg_end; ++t)
-                tile_hits[t]++;
-            const int kvh = unit / g.ngroups, grp = unit % g.ngroups;
+            for (int t = sg.t0; t < sg.t1; ++t)
+                tile_hits[{r, sg.unit, t}]++;
+            const int kvh = sg.unit / g.ngroups, grp = sg.unit % g.ngroups;
             pieces[{r, kvh, grp}].push_back({wg, slot, whole});
             if (!whole) {
                 if (!slots_used.insert({wg, slot}).second) {
@@ -77,20 +84,26 @@ int main()
                     return 1;
                 }
                 // a partial piece must be the first or the last segment of the run
-                if (!(seg == 0 || seg_end == end)) {
+                if (!(seg == 0 || sg.next == end)) {
                     printf("FAIL partial segment in the middle of a run\n");
                     return 1;
                 }
             }
-            pos = seg_end;
             ++seg;
         }
     }
-    for (int64_t t = 0; t < total; ++t)
-        if (tile_hits[t] != 1) {
-            printf("FAIL tile %lld hit %d times\n", (long long)t, tile_hits[t]);
-            return 1;
-        }
+    for (int r = 0; r < d.B; ++r) {
+        ReqGeom g = req_geom(L[r], n[r], d);
+        for (int u = 0; u < (g.ngroups ? d.Hkv * g.ngroups : 0); ++u)
+            for (int t = 0; t < g.ntiles; ++t) {
+                auto it = tile_hits.find({r, u, t});
+                const int hits = it == tile_hits.end() ? 0 : it->second;
+                if (hits != 1) {
+                    printf("FAIL request %d unit %d tile %d hit %d times\n", r, u, t, hits);
+                    return 1;
+                }
+            }
+    }
     int split = 0;
     size_t max_pieces = 0;
     for (int r = 0; r < d.B; ++r) {
@@ -99,9 +112,9 @@ int main()
             for (int grp = 0; grp < g.ngroups; ++grp) {
                 auto& pl = pieces[{r, kvh, grp}];
                 const int unit = kvh * g.ngroups + grp;
-                const int64_t us = rbase[r] + (int64_t)unit * g.ntiles;
-                const int64_t ue = us + g.ntiles;
-                const int64_t kf = us / tpw, kl = (ue - 1) / tpw;
+                const int64_t us = rbase[r] + (int64_t)unit * g.uwork;
+                int64_t kf, kl;
+                unit_pieces(g, us, d.ov, tpw, kf, kl);
                 if (kf == kl) {
                     if (pl.size() != 1 || !std::get<2>(pl[0])) {
                         printf("FAIL unit not whole in one workgroup\n");
@@ -116,7 +129,7 @@ int main()
                     return 1;
                 }
                 for (int64_t k = kf; k <= kl; ++k) {
-                    const int slot = (k == kf && us != k * tpw) ? 1 : 0;  // the combine's rule
+                    const int slot = piece_slot(k, us, tpw);  // the combine's rule
                     bool found = false;
                     for (auto& p : pl)
                         if (std::get<0>(p) == k && std::get<1>(p) == slot && !std::get<2>(p))

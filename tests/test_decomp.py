@@ -20,8 +20,8 @@ def checker(tmp_path_factory):
     return exe
 
 
-def run(exe, L, n, Hkv, G, window, rmax, tk, P):
-    text = f"{len(L)} {Hkv} {G} {window} {rmax} {tk} {P}\n" + "\n".join(f"{a} {b}" for a, b in zip(L, n)) + "\n"
+def run(exe, L, n, Hkv, G, window, rmax, tk, P, ov=0):
+    text = f"{len(L)} {Hkv} {G} {window} {rmax} {tk} {P} {ov}\n" + "\n".join(f"{a} {b}" for a, b in zip(L, n)) + "\n"
     r = subprocess.run([exe], input=text, capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.startswith("OK"), r.stdout + r.stderr
     return [int(x) for x in r.stdout.split()[1:]]
@@ -37,7 +37,8 @@ def test_config_shapes(checker, name, P):
     k = ks[rng.integers(0, len(ks), size=cfg.B)] if len(ks) > 1 else np.full(cfg.B, ks[0])
     G = cfg.Hq // cfg.Hkv
     for rmax, tk in ((80, 32), (64, 32), (16, 16)):
-        run(checker, L, 1 + k, cfg.Hkv, G, cfg.window, rmax, tk, P)
+        for ov in (0, 3):
+            run(checker, L, 1 + k, cfg.Hkv, G, cfg.window, rmax, tk, P, ov)
 
 
 def test_random_edge_cases(checker):
@@ -53,7 +54,8 @@ def test_random_edge_cases(checker):
         rmax = int(rng.choice([16, 32, 48, 64, 80]))
         tk = int(rng.choice([16, 32]))
         P = int(rng.integers(1, 60))
-        run(checker, L, n, Hkv, G, window, rmax, tk, P)
+        ov = int(rng.choice([0, 0, 1, 3, 7]))
+        run(checker, L, n, Hkv, G, window, rmax, tk, P, ov)
 
 
 def test_all_empty_requests(checker):
