@@ -287,28 +287,6 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
             // address the row start instead (never past the row), and are zeroed
             const int64_t head_off = (int64_t)kvh * D;
 
-            // ---------------- Q^T (B operand) for the unit ----------------
-            bf16x8_t qf[RT][KS];
-#pragma unroll
-            for (int b = 0; b < RT; ++b) {
-                const int32_t row = b * 16 + l16;
-                const bool rv = row < rows_here;
-                const int32_t rr = row0 + (rv ? row : 0);
-                const int32_t qi = rr / G;
-                const int32_t qj = rr % G;
-                const uint16_t* qrow = a.q + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    u32x4_t x = ldg16(qrow + (dval[s] ? wbase + 32 * s + 8 * grp4 : 0));
-                    const bool keep = rv && dval[s];
-                    x[0] = keep ? x[0] : 0u;
-                    x[1] = keep ? x[1] : 0u;
-                    x[2] = keep ? x[2] : 0u;
-                    x[3] = keep ? x[3] : 0u;
-                    qf[b][s] = as_bf16x8(x);
-                }
-            }
-
             // Element offset of the request's first visible key row: keys past the end (and
             // tiles past the segment) read it, so every load stays in bounds and finite.
             const int64_t safe_row =
@@ -348,6 +326,35 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     rows[i] = key < kend ? row : safe_row;
                 }
             };
+
+            // Page entries of the segment's first two tiles, requested before Q so that
+            // waiting for them never waits for Q (which is needed only at the first product).
+            const int32_t pg_first = tile_page(t0);
+            const int32_t pg_second = tile_page(t0 + 1);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---------------- Q^T (B operand) for the unit ----------------
+            bf16x8_t qf[RT][KS];
+#pragma unroll
+            for (int b = 0; b < RT; ++b) {
+                const int32_t row = b * 16 + l16;
+                const bool rv = row < rows_here;
+                const int32_t rr = row0 + (rv ? row : 0);
+                const int32_t qi = rr / G;
+                const int32_t qj = rr % G;
+                const uint16_t* qrow = a.q + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    u32x4_t x = ldg16(qrow + (dval[s] ? wbase + 32 * s + 8 * grp4 : 0));
+                    const bool keep = rv && dval[s];
+                    x[0] = keep ? x[0] : 0u;
+                    x[1] = keep ? x[1] : 0u;
+                    x[2] = keep ? x[2] : 0u;
+                    x[3] = keep ? x[3] : 0u;
+                    qf[b][s] = as_bf16x8(x);
+                }
+            }
+
 
             float m_fix[NOWN];
             // Visible key range [rlo, rhi] of this lane's query row in each owned row tile, and
@@ -406,24 +413,23 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 
                 // One 32-key tile per step.  At the top of step t the registers holding the
                 // K/V of tile t are written to LDS and at once refilled with tile t+1, which
-                // so has a whole step to arrive.  Every request is unconditional (a tile
-                // past the segment reads the safe row, page entries are read at clamped
-                // indices): the loop has no divergent branches and each wait on the memory
-                // counter is exact.  The issue order (page entries, V, K) is pinned with
+                // so has a whole step to arrive.  Inside the loop every request is
+                // unconditional (keys past the request read the safe row, page entries are
+                // read at clamped indices): the loop has no divergent branches and each wait
+                // on the memory counter is exact.  The issue order (page entries, V, K) is pinned with
                 // scheduling barriers, here and in the loop: the compiler's waits at the
                 // loop head are exact only if both paths into it issue in the same order.
-                tile_rows(t0, tile_page(t0), rows);
-                pg_next = tile_page(t0 + 1);
+                tile_rows(t0, pg_first, rows);
+                pg_next = pg_second;
                 __builtin_amdgcn_sched_barrier(0);
                 issue(a.k_pages, kr);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (MODE != kMaxScan)
                     issue(a.v_pages, vr);
                 __builtin_amdgcn_sched_barrier(0);
-                // An abandoned lazy segment leaves by the loop condition only: an exit between
-                // the softmax and the PV product would make the compiler keep a second copy of
-                // every accumulator.  The tile that triggered it still runs its (discarded) PV.
-                for (int32_t t = t0; t < t1 && !aborted; ++t) {
+                // One tile; PF: also request the next one (every tile but the segment's last).
+                auto step = [&](const int32_t t, auto pf_tag) {
+                    constexpr bool PF = decltype(pf_tag)::value;
                     const int32_t k0 = g.kv_lo + t * kTK;
                     // (1) this wave's K and V slices -> LDS [key][d_local].  Keys past the
                     // request hold the safe row and d past head_dim the row start: finite
@@ -438,10 +444,12 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                         *reinterpret_cast<u32x4_t*>(kls + C::kofs(i * KPI + kl, sl)) = kr[i];
                     // request tile t+1 (page entries of t+2 first, so that waiting for them
                     // later never waits for K/V)
-                    tile_rows(t + 1, pg_next, rows);
-                    pg_next = tile_page(t + 2);
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue(a.k_pages, kr);
+                    if constexpr (PF) {
+                        tile_rows(t + 1, pg_next, rows);
+                        pg_next = tile_page(t + 2);
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue(a.k_pages, kr);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                     // (2) partial S^T over this wave's d-slice (absent d: Q is zero there and K
                     //     finite; absent keys are masked below).  A operand: key 16h + l16,
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     __syncthreads();
                     // V of tile t+1: requested here rather than with K so that the two
                     // halves of the workgroup's 64 KB do not queue at the address unit at once
-                    if constexpr (MODE != kMaxScan)
+                    if constexpr (MODE != kMaxScan && PF)
                         issue(a.v_pages, vr);
                     __builtin_amdgcn_sched_barrier(0);
                     // (3) owners: reduce, mask, softmax, publish P^T
@@ -551,7 +559,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     }
                     __syncthreads();
                     if constexpr (MODE == kMaxScan)
-                        continue;
+                        return;
                     if constexpr (MODE == kLazy) {
                         int anyover = 0;
 #pragma unroll
@@ -583,7 +591,17 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                         for (int b = 0; b < RT; ++b)
                             o[c][b] = mfma16(vb, pb[b], o[c][b]);
                     }
-                }
+                };
+                // An abandoned lazy segment leaves by the loop condition only: an exit between
+                // the softmax and the PV product would make the compiler keep a second copy of
+                // every accumulator.  The tile that triggered it still runs its (discarded) PV.
+                int32_t t = t0;
+                for (; t + 1 < t1 && !aborted; ++t)
+                    step(t, std::true_type{});
+                // The last tile requests nothing: a request for a tile past the segment would
+                // hold its registers, and so the epilogue, until it landed.
+                if (t < t1 && !aborted)
+                    step(t, std::false_type{});
                 // wait for the last tile's LDS traffic of every wave before anything reuses it
                 __syncthreads();
                 return aborted;
