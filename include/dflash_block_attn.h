@@ -107,7 +107,9 @@ typedef struct {
  *   stream      hipStream_t to enqueue on (NULL = null stream)
  *   desc        host struct above
  *
- * Output rows are rounded to bf16 with round-to-nearest-even from fp32 accumulation.
+ * Output rows are rounded to bf16 with round-to-nearest-even from fp32 accumulation.  When a
+ * request's keys are split over several workgroups, each piece's normalised output is kept in
+ * bf16 in the workspace (with an fp32 log-sum-exp) and the pieces are merged in fp32.
  * The call is asynchronous: it validates, enqueues one attention kernel and, when
  * some request's keys were split over several workgroups, one combine kernel, and
  * returns.  Buffers must stay valid until the stream has run the work.  Concurrent

@@ -198,7 +198,7 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             p->ov = kSegmentCharge;
     }
     if (p->P > 1) {
-        const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(float);
+        const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(uint16_t);  // bf16 partials
         p->off_lse = align_up(o_bytes);
         p->ws_bytes = p->off_lse + align_up((size_t)p->P * 2 * p->rmax * sizeof(float));
         p->combine_wgs = dflash::combine_grid((int64_t)desc->total_q * Hq);
@@ -263,7 +263,7 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.spans = span_offsets ? spans : nullptr;
     a.num_spans = span_offsets ? num_spans : 0;
     a.out = static_cast<uint16_t*>(out);
-    a.part_o = p.ws_bytes ? static_cast<float*>(desc->workspace) : nullptr;
+    a.part_o = p.ws_bytes ? static_cast<uint16_t*>(desc->workspace) : nullptr;
     a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(desc->workspace) + p.off_lse) : nullptr;
     a.d.B = desc->num_reqs;
     a.d.Hkv = n_kv_heads;

@@ -163,6 +163,11 @@ struct Cfg {
     static constexpr int OFF_MREF = OFF_LSUM + ROWF_BYTES;
     static constexpr int OFF_FLAG = OFF_MREF + ROWF_BYTES;
     static constexpr int LDS_BYTES = OFF_FLAG + 16 * 4;
+    // Epilogue staging of the unit's normalised rows as bf16, [row][d] with a 32-byte
+    // pad per row, in the bytes the tile loop no longer uses (everything below LSUM).
+    static constexpr int SROW = DP * 2 + 32;
+    static constexpr int OFF_STAGE = 0;
+    static_assert(ROWS * SROW <= OFF_LSUM, "epilogue staging must fit below the row sums");
     static_assert(KS >= 1 && DT >= 1, "head_dim too small for the d-split");
     static_assert(NCH >= 4 && NCH <= 16 && KPI * NCH == 64 && NI * KPI == kTK, "load geometry");
     static_assert(RT <= 16, "flag array");
@@ -635,33 +640,60 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 }
             }
             __syncthreads();
-            const int64_t sbase = ((int64_t)wg * 2 + slot) * d.rmax;
+            // Stage the normalised rows as bf16 (rows [row][d]) in the LDS the tile loop no
+            // longer uses, then write whole rows with contiguous 16-byte-per-lane stores: a
+            // store straight from the MFMA layout would scatter 16 short row pieces.
+            unsigned char* stage = lds + C::OFF_STAGE;
 #pragma unroll
             for (int b = 0; b < RT; ++b) {
-                const int32_t row = b * 16 + l16;
-                if (row < rows_here) {
-                    const float l = lsum_s[row];
-                    const float inv = l > 0.f ? 1.f / l : 0.f;
-                    const int32_t rr = row0 + row;
-                    const int32_t qi = rr / G;
-                    const int32_t qj = rr % G;
-                    uint16_t* orow = a.out + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
-                    float* prow = a.part_o + (sbase + row) * a.Dp;
+                const float l = lsum_s[b * 16 + l16];
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+                unsigned char* srow = stage + (b * 16 + l16) * C::SROW + (wbase + 4 * grp4) * 2;
 #pragma unroll
-                    for (int c = 0; c < DT; ++c) {
-                        const int32_t dd = wbase + 16 * c + 4 * grp4;
-                        if (dd < D) {
-                            const f32x4_t v = o[c][b] * inv;
-                            if (whole) {
-                                const u32x2_t pk2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                                *reinterpret_cast<u32x2_t*>(orow + dd) = pk2;
-                            } else {
-                                *reinterpret_cast<f32x4_t*>(prow + dd) = v;
-                            }
-                        }
+                for (int c = 0; c < DT; ++c) {
+                    const f32x4_t v = o[c][b] * inv;
+                    const u32x2_t pk2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                    *reinterpret_cast<u32x2_t*>(srow + 32 * c) = pk2;
+                }
+            }
+            __syncthreads();
+            constexpr int CPR = DP / 8;    // 16-byte chunks per row
+            constexpr int RPI = 64 / CPR;  // rows per wave instruction
+            const int rsub = lane / CPR;
+            const int ch = lane % CPR;
+            if (!whole) {
+                // A partial: bf16 rows of this workgroup's slot (a normalised partial is a
+                // convex combination of bf16 values, so bf16 holds its range; its rounding
+                // is that of the output itself).  Padding rows and head-dim columns past D
+                // land in the slot's own rows and row padding, which the combine never
+                // reads, so no store needs a predicate.
+                const int64_t sbase = ((int64_t)wg * 2 + slot) * d.rmax;
+#pragma unroll
+                for (int r0 = wave * RPI; r0 < C::ROWS; r0 += WAVES * RPI) {
+                    const int row = r0 + rsub;
+                    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + row * C::SROW + ch * 16);
+                    *reinterpret_cast<u32x4_t*>(a.part_o + (sbase + row) * DP + ch * 8) = x;
+                }
+                if (wave == 0 && grp4 == 0) {
+#pragma unroll
+                    for (int b = 0; b < RT; ++b) {
+                        const float l = lsum_s[b * 16 + l16];
+                        a.part_lse[sbase + b * 16 + l16] = l > 0.f ? mref_s[b * 16 + l16] + log2f(l) : -INFINITY;
                     }
-                    if (!whole && wave == 0 && grp4 == 0)
-                        a.part_lse[sbase + row] = l > 0.f ? mref_s[row] + log2f(l) : -INFINITY;
+                }
+            } else {
+                // The whole unit was here: bf16 output rows, real rows and columns only.
+#pragma unroll
+                for (int r0 = wave * RPI; r0 < C::ROWS; r0 += WAVES * RPI) {
+                    const int row = r0 + rsub;
+                    if (row < rows_here && (EXACT || ch * 8 < D)) {
+                        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + row * C::SROW + ch * 16);
+                        const int32_t rr = row0 + row;
+                        const int32_t qi = rr / G;
+                        const int32_t qj = rr % G;
+                        uint16_t* orow = a.out + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
+                        *reinterpret_cast<u32x4_t*>(orow + ch * 8) = x;
+                    }
                 }
             }
             __syncthreads();

@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
                     if (whole)
                         a.out[((qstart + i) * a.Hq + (int64_t)kvh * G + j) * D + dd] = f32_to_bf16(o[rho][c] * inv);
                     else
-                        a.part_o[(sbase + rho) * a.Dp + dd] = o[rho][c] * inv;
+                        a.part_o[(sbase + rho) * a.Dp + dd] = f32_to_bf16(o[rho][c] * inv);
                 }
             }
             if (!whole && tid == 0)

@@ -17,6 +17,7 @@
 namespace dflash {
 
 constexpr int kCombineRowsPerWg = 4;  // one wave each
+constexpr int kPiecesPerStep = 16;   // partial rows requested together by each lane
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 {
@@ -30,16 +31,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int32_t h = (int32_t)(row % a.Hq);
 
     int32_t r;
-    int64_t qstart;
-    wave_find_token(a.block_lens, d.B, t, r, qstart);
+    int64_t qstart, rbase, total;
+    wave_locate_token(a.ctx_lens, a.block_lens, d, t, r, qstart, rbase, total);
     if (r >= d.B)
         return;  // token past the real total
     const int32_t L = a.ctx_lens[r];
     const int32_t n = a.block_lens[r];
     const ReqGeom g = req_geom(L, n, d);
-    const int64_t total = wave_total_work(a.ctx_lens, a.block_lens, d);
     const int64_t tpw = tiles_per_wg(total, d.P);
-    const int64_t rbase = wave_work_before(a.ctx_lens, a.block_lens, d, r);
 
     const int32_t i = (int32_t)(t - qstart);
     const int32_t kvh = h / d.G;
@@ -54,67 +53,62 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     if (kf == kl)
         return;  // finished inside one workgroup, already written
 
-    // piece weights, lane-parallel: lane j holds piece kf + j (+ 64 per round)
+    // Lane j holds piece kf + j (+ 64 per round).  The log-sum-exps and the partial rows
+    // are requested together (rows of pieces that saw no key hold zeros, so they need no
+    // guard), and the weights are formed once everything has arrived.
     const int64_t npieces = kl - kf + 1;
-    float M = -INFINITY;
-    for (int64_t base = 0; base < npieces; base += 64) {
-        const int64_t k = kf + base + lane;
-        if (k <= kl) {
-            const int slot = piece_slot(k, us, tpw);
-            M = fmaxf(M, a.part_lse[(k * 2 + slot) * d.rmax + rin]);
-        }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        M = fmaxf(M, __shfl_xor(M, off));
-
     const int32_t d0 = lane * 8;
     const bool dlive = d0 < a.D;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         acc[e] = 0.f;
+    float M = -INFINITY;
     float W = 0.f;
     for (int64_t base = 0; base < npieces; base += 64) {
         const int64_t kq = kf + base + lane;
-        float wl = 0.f;
-        if (kq <= kl) {
-            const int slot = piece_slot(kq, us, tpw);
-            const float lse = a.part_lse[(kq * 2 + slot) * d.rmax + rin];
-            wl = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
-        }
-        W += wl;
+        const float lse = kq <= kl ? a.part_lse[(kq * 2 + piece_slot(kq, us, tpw)) * d.rmax + rin] : -INFINITY;
         const int cnt = (int)min<int64_t>(64, npieces - base);
-        // four pieces per step keep eight 16-byte loads of each lane in flight
-        for (int j0 = 0; j0 < cnt; j0 += 4) {
-            float wj[4];
-            float4 x0[4], x1[4];
+        float wl = 0.f;
+        for (int j0 = 0; j0 < cnt; j0 += kPiecesPerStep) {
+            uint4 x[kPiecesPerStep];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = min(j0 + u, cnt - 1);
-                wj[u] = (j0 + u < cnt) ? __shfl(wl, j) : 0.f;
-                const int64_t k = kf + base + j;
-                const int slot = piece_slot(k, us, tpw);
-                const int64_t prow = (k * 2 + slot) * d.rmax + rin;
-                if (dlive && wj[u] != 0.f) {
-                    const float4* src = reinterpret_cast<const float4*>(a.part_o + prow * a.Dp + d0);
-                    x0[u] = src[0];
-                    x1[u] = src[1];
-                } else {
-                    x0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    x1[u] = x0[u];
+            for (int u = 0; u < kPiecesPerStep; ++u) {
+                const int jj = min(j0 + u, cnt - 1);
+                const int64_t k = kf + base + jj;
+                const int64_t prow = (k * 2 + piece_slot(k, us, tpw)) * d.rmax + rin;
+                x[u] = (dlive && j0 + u < cnt) ? *reinterpret_cast<const uint4*>(a.part_o + prow * a.Dp + d0)
+                                               : make_uint4(0, 0, 0, 0);
+            }
+            if (j0 == 0) {
+                // weights of this round, formed while the rows above are in flight; what
+                // earlier rounds summed (more than 64 pieces only) is rescaled to the new max
+                float mr = lse;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1)
+                    mr = fmaxf(mr, __shfl_xor(mr, off));
+                const float m_new = fmaxf(M, mr);
+                if (base > 0 && m_new > M) {
+                    const float sc = exp2f(M - m_new);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[e] *= sc;
+                    W *= sc;
                 }
+                M = m_new;
+                wl = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
+                W += wl;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                acc[0] = fmaf(wj[u], x0[u].x, acc[0]);
-                acc[1] = fmaf(wj[u], x0[u].y, acc[1]);
-                acc[2] = fmaf(wj[u], x0[u].z, acc[2]);
-                acc[3] = fmaf(wj[u], x0[u].w, acc[3]);
-                acc[4] = fmaf(wj[u], x1[u].x, acc[4]);
-                acc[5] = fmaf(wj[u], x1[u].y, acc[5]);
-                acc[6] = fmaf(wj[u], x1[u].z, acc[6]);
-                acc[7] = fmaf(wj[u], x1[u].w, acc[7]);
+            for (int u = 0; u < kPiecesPerStep; ++u) {
+                const float wj = (j0 + u < cnt) ? __shfl(wl, min(j0 + u, cnt - 1)) : 0.f;
+                const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // bf16 -> fp32 is exact: the bits move to the high half
+                    acc[2 * e] = fmaf(wj, __uint_as_float(w4[e] << 16), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(wj, __uint_as_float(w4[e] & 0xffff0000u), acc[2 * e + 1]);
+                }
             }
         }
     }

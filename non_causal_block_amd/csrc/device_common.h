@@ -136,6 +136,43 @@ __device__ __forceinline__ int64_t wave_work_before(const int32_t* __restrict__ 
     return acc;
 }
 
+// One pass over the request arrays, 64 requests per step (one load round for up to
+// 64 requests): the request holding packed query token t with its first token, the
+// flat work before it, and the call's total work.  r_out = B for a token past the
+// end.  Wave-uniform.
+__device__ __forceinline__ void wave_locate_token(const int32_t* __restrict__ ctx_lens,
+                                                  const int32_t* __restrict__ block_lens, const Decomp& d, int64_t t,
+                                                  int32_t& r_out, int64_t& qstart_out, int64_t& wbefore_out,
+                                                  int64_t& total_out)
+{
+    const int lane = threadIdx.x & 63;
+    int64_t qcarry = 0, wcarry = 0;
+    bool found = false;
+    r_out = d.B;
+    qstart_out = 0;
+    wbefore_out = 0;
+    for (int32_t base = 0; base < d.B; base += 64) {
+        const int32_t r = base + lane;
+        const bool live = r < d.B;
+        const int32_t L = live ? ctx_lens[r] : 0;
+        const int32_t n = live ? block_lens[r] : 0;
+        const int64_t w = live ? req_work(req_geom(L, n, d), d) : 0;
+        const int64_t qincl = wave_inclusive_scan((int64_t)n) + qcarry;
+        const int64_t wincl = wave_inclusive_scan(w) + wcarry;
+        const unsigned long long m = __ballot(qincl > t);
+        if (!found && m) {
+            const int src = __ffsll((long long)m) - 1;
+            r_out = base + src;
+            qstart_out = shfl_i64(qincl - n, src);
+            wbefore_out = shfl_i64(wincl - w, src);
+            found = true;
+        }
+        qcarry = shfl_i64(qincl, 63);
+        wcarry = shfl_i64(wincl, 63);
+    }
+    total_out = wcarry;
+}
+
 // Logical workgroup index: consecutive logical indices are placed on the same XCD
 // (the dispatcher deals workgroups round-robin over 8 XCDs), so the workgroups
 // that share a unit share that XCD's L2 for the unit's Q rows.
@@ -160,7 +197,7 @@ struct AttnArgs {
     const int32_t* spans;         // [num_spans][2] (start, end) key positions
     int32_t num_spans;
     uint16_t* out;
-    float* part_o;     // [P][2][rmax][Dp]
+    uint16_t* part_o;  // bf16 [P][2][rmax][Dp]: normalised partial outputs
     float* part_lse;   // [P][2][rmax]
     Decomp d;
     int32_t Hq;
@@ -174,7 +211,7 @@ struct AttnArgs {
 struct CombineArgs {
     const int32_t* ctx_lens;
     const int32_t* block_lens;
-    const float* part_o;
+    const uint16_t* part_o;  // bf16 [P][2][rmax][Dp]
     const float* part_lse;
     uint16_t* out;
     Decomp d;

@@ -214,6 +214,17 @@ def test_split_invariance():
         assert float(np.max(diff)) <= 4e-3, (nwg, float(np.max(diff)))
 
 
+def test_combine_over_more_than_64_pieces():
+    """A unit split over hundreds of workgroups: the combine merges its pieces in
+    rounds of 64 (rescaling earlier rounds to the running maximum).  One long request
+    and one kv-head, so 600 workgroups take about one tile each."""
+    wl = workloads.build(2, 8, 1, 128, [8000, 300], [9, 5], [0, 1], seed=31)
+    ref = oracle.run_workload(wl)
+    for nwg in (150, 600):
+        got = H.to_f64(H.run(wl, num_workgroups=nwg))
+        H.assert_parity(got, ref, f"many pieces wg={nwg}")
+
+
 def test_page_permutation_invariance_is_bitwise():
     a = workloads.make("c2_paged_d256", ctx_cap=1200)
     b = workloads.build(a.B, a.Hq, a.Hkv, a.D, a.ctx_lens, a.block_lens, a.causal, seed=999, extra_pages=5)
