@@ -205,6 +205,39 @@ const char* dflash_last_error_message(void);
 int dflash_abi_version(void);
 
 /*
+ * Debug checks of device-side values.  Lengths, page ids and span offsets live in
+ * device memory, so the host cannot check them, and out-of-range values are
+ * undefined behaviour on the normal path.  With checks on, every attention / append
+ * call first runs a one-workgroup kernel over them.  On a failure it sets bits in a
+ * sticky per-device state word, and every kernel of that call then does nothing:
+ * `out`, the pages and the workspace are left untouched, and no bad page id is
+ * dereferenced.  The checks cost one small launch per call.  They are off unless
+ * DFLASH_DEBUG_CHECKS=1 is in the environment at the first call.
+ *
+ * Bits: a request's pages are those a kernel of the call reads or writes, i.e. from
+ * the first key the attention reads (window start, tile-aligned) or from the block
+ * start for an append alone, to the request's last key.
+ */
+#define DFLASH_DEBUG_NEGATIVE_LENGTH   1u  /* ctx_lens[r] < 0 or block_lens[r] < 0                     */
+#define DFLASH_DEBUG_BEYOND_PAGE_TABLE 2u  /* L + n > max_pages_per_req * page_size                     */
+#define DFLASH_DEBUG_BAD_PAGE_ID       4u  /* a page the call touches is outside [0, desc->num_pages)   */
+#define DFLASH_DEBUG_TOTAL_Q_MISMATCH  8u  /* sum(block_lens) != desc->total_q                          */
+#define DFLASH_DEBUG_ABOVE_HINT       16u  /* a block above max_block_len, or sum(L+n) > total_kv_len   */
+#define DFLASH_DEBUG_BAD_SPAN_OFFSETS 32u  /* span_offsets not non-decreasing within [0, num_spans]     */
+
+/* Switches the checks on (non-zero) or off for later calls; returns the previous setting. */
+int dflash_set_debug_checks(int on);
+
+/*
+ * Synchronises the current device, stores the OR of the bits set by all checked calls
+ * since the last query in *bits, and stores the lowest failing request index in
+ * *first_request (-1 when no bit is set).  Then it clears the state.  Calls whose checks
+ * fail do nothing, so with checks on a non-zero result means some call was skipped.
+ * Returns DFLASH_ERR_HIP without a device.
+ */
+int dflash_debug_checks_result(uint32_t* bits, int32_t* first_request);
+
+/*
  * DFlash2 in-block grouped dynamic depthwise convolution (prhub summary of vLLM
  * PR #52816, "DFlash2: local convolution + candidate selector", section
  * "motivation"): for every request's block of n positions and every channel c,

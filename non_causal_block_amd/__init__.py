@@ -48,6 +48,28 @@ def dflash_abi_version() -> int:
     return _lib.load().dflash_abi_version()
 
 
+# bits of dflash_debug_checks_result (include/dflash_block_attn.h)
+DFLASH_DEBUG_NEGATIVE_LENGTH = 1
+DFLASH_DEBUG_BEYOND_PAGE_TABLE = 2
+DFLASH_DEBUG_BAD_PAGE_ID = 4
+DFLASH_DEBUG_TOTAL_Q_MISMATCH = 8
+DFLASH_DEBUG_ABOVE_HINT = 16
+DFLASH_DEBUG_BAD_SPAN_OFFSETS = 32
+
+
+def dflash_set_debug_checks(on: bool) -> bool:
+    """Switch the device-side value checks for later calls; returns the previous setting."""
+    return bool(_lib.load().dflash_set_debug_checks(1 if on else 0))
+
+
+def dflash_debug_checks_result():
+    """(bits, first_request) of the checked calls since the last query; synchronises and clears."""
+    bits = ctypes.c_uint32(0)
+    req = ctypes.c_int32(-1)
+    _check(_lib.load().dflash_debug_checks_result(ctypes.byref(bits), ctypes.byref(req)))
+    return bits.value, req.value
+
+
 def dflash_block_conv(x, base, delta, block_lens, num_reqs: int, total_q: int, channels: int, groups: int,
                        taps: int, out, stream: Optional[int]) -> int:
     """Raw call: DFlash2 in-block grouped dynamic depthwise convolution; status code out."""

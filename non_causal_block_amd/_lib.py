@@ -97,5 +97,9 @@ def load() -> ctypes.CDLL:
     lib.dflash_block_conv.restype = ctypes.c_int
     lib.dflash_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.dflash_stream_read.restype = ctypes.c_int
+    lib.dflash_set_debug_checks.argtypes = [ctypes.c_int]
+    lib.dflash_set_debug_checks.restype = ctypes.c_int
+    lib.dflash_debug_checks_result.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32)]
+    lib.dflash_debug_checks_result.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -8,8 +8,10 @@
 // code", the non-causal assertion and its message).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -32,6 +34,34 @@ int fail(int status, const char* fmt, ...)
 }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Debug checks of device-side values: off unless DFLASH_DEBUG_CHECKS=1 in the
+// environment at the first call, or switched by dflash_set_debug_checks.
+std::atomic<int> g_debug_checks{-1};
+
+bool debug_checks_on()
+{
+    int v = g_debug_checks.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char* e = std::getenv("DFLASH_DEBUG_CHECKS");
+        const int want = (e && e[0] == '1') ? 1 : 0;
+        int expected = -1;
+        g_debug_checks.compare_exchange_strong(expected, want);
+        v = g_debug_checks.load(std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+
+// The debug state word of the current device when checks are on, else nullptr.
+int debug_state(uint32_t** out)
+{
+    *out = nullptr;
+    if (!debug_checks_on())
+        return DFLASH_OK;
+    if (dflash::debug_state_ptr(out) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "debug checks: cannot locate the device state word");
+    return DFLASH_OK;
+}
 
 int ilog2(int64_t x)
 {
@@ -210,7 +240,32 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
 struct AttnCall {
     Plan plan;
     dflash::AttnArgs args;
+    dflash::ValidateArgs check;  // used when args.dbg is set
 };
+
+dflash::ValidateArgs validate_args(const int32_t* page_table, const int32_t* ctx_lens, const int32_t* block_lens,
+                                   const int32_t* span_offsets, int32_t num_spans, int32_t window, int32_t tile_keys,
+                                   bool from_block, const dflash_batch_desc* desc, uint32_t* state)
+{
+    dflash::ValidateArgs v;
+    v.page_table = page_table;
+    v.ctx_lens = ctx_lens;
+    v.block_lens = block_lens;
+    v.span_offsets = span_offsets;
+    v.B = desc->num_reqs;
+    v.page_size = desc->page_size;
+    v.max_pages_per_req = desc->max_pages_per_req;
+    v.window = window;
+    v.tile_keys = tile_keys > 0 ? tile_keys : 1;
+    v.from_block = from_block ? 1 : 0;
+    v.num_pages = desc->num_pages;
+    v.total_q = desc->total_q;
+    v.max_block_len = desc->max_block_len;
+    v.num_spans = span_offsets ? num_spans : 0;
+    v.total_kv_len = desc->total_kv_len;
+    v.state = state;
+    return v;
+}
 
 int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
                  const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
@@ -279,13 +334,26 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.page_shift = ilog2(desc->page_size);
     a.max_pages_per_req = desc->max_pages_per_req;
     a.scale_log2 = scale * 1.4426950408889634f;
+    uint32_t* dbg = nullptr;
+    st = debug_state(&dbg);
+    if (st != DFLASH_OK)
+        return st;
+    a.dbg = dbg;
+    if (dbg)
+        call->check = validate_args(page_table, ctx_lens, block_lens, span_offsets, num_spans, window, p.tk, false,
+                                    desc, dbg);
     return DFLASH_OK;
 }
 
-int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t s)
+int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t s, bool validate = true)
 {
     const Plan& p = call.plan;
     const dflash::AttnArgs& a = call.args;
+    if (a.dbg && validate) {
+        const hipError_t ev = dflash::launch_validate(call.check, s);
+        if (ev != hipSuccess)
+            return fail(DFLASH_ERR_HIP, "debug-check kernel launch failed: %s", hipGetErrorString(ev));
+    }
     if (desc->event_attn_begin && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_begin), s) != hipSuccess)
         return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_begin) failed");
     hipError_t e = p.kernel == DFLASH_KERNEL_MFMA ? dflash::launch_attn_mfma(a, p.Dp, p.row_tiles, s)
@@ -306,6 +374,7 @@ int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t
         c.D = a.D;
         c.Dp = p.Dp;
         c.total_rows = (int64_t)desc->total_q * a.Hq;
+        c.dbg = a.dbg;
         e = dflash::launch_combine(c, p.combine_wgs, s);
         if (e != hipSuccess)
             return fail(DFLASH_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
@@ -354,6 +423,11 @@ int append_prepare(const void* k_new, const void* v_new, void* k_pages, void* v_
     a->D = head_dim;
     a->page_shift = ilog2(desc->page_size);
     a->max_pages_per_req = desc->max_pages_per_req;
+    uint32_t* dbg = nullptr;
+    st = debug_state(&dbg);
+    if (st != DFLASH_OK)
+        return st;
+    a->dbg = dbg;
     return DFLASH_OK;
 }
 
@@ -438,6 +512,33 @@ const char* dflash_status_string(int status)
 
 const char* dflash_last_error_message(void) { return g_last_error; }
 
+int dflash_set_debug_checks(int on)
+{
+    const int prev = debug_checks_on() ? 1 : 0;
+    g_debug_checks.store(on ? 1 : 0, std::memory_order_relaxed);
+    return prev;
+}
+
+int dflash_debug_checks_result(uint32_t* bits, int32_t* first_request)
+{
+    if (!bits || !first_request)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "debug checks: bits and first_request must be non-NULL");
+    uint32_t* p = nullptr;
+    if (dflash::debug_state_ptr(&p) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "debug checks: cannot locate the device state word");
+    if (hipDeviceSynchronize() != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "debug checks: hipDeviceSynchronize failed");
+    uint32_t host[2] = {0, 0};
+    if (hipMemcpy(host, p, sizeof host, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "debug checks: reading the state word failed");
+    const uint32_t clear[2] = {0u, 0x7fffffffu};
+    if (hipMemcpy(p, clear, sizeof clear, hipMemcpyHostToDevice) != hipSuccess)
+        return fail(DFLASH_ERR_HIP, "debug checks: clearing the state word failed");
+    *bits = host[0];
+    *first_request = host[0] ? (int32_t)host[1] : -1;
+    return DFLASH_OK;
+}
+
 int dflash_block_attn_supports(int32_t n_heads, int32_t n_kv_heads, int32_t head_dim)
 {
     char saved[sizeof g_last_error];
@@ -515,6 +616,13 @@ int dflash_block_kv_append(const void* k_new, const void* v_new, void* k_pages, 
                                   head_dim, desc, &a);
     if (st != DFLASH_OK || a.total_rows == 0)
         return st;
+    if (a.dbg) {
+        const dflash::ValidateArgs v =
+            validate_args(page_table, ctx_lens, block_lens, nullptr, 0, 0, 1, true, desc, const_cast<uint32_t*>(a.dbg));
+        const hipError_t ev = dflash::launch_validate(v, static_cast<hipStream_t>(stream));
+        if (ev != hipSuccess)
+            return fail(DFLASH_ERR_HIP, "debug-check kernel launch failed: %s", hipGetErrorString(ev));
+    }
     const hipError_t e = dflash::launch_kv_append(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DFLASH_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
@@ -538,6 +646,15 @@ int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new
     if (st != DFLASH_OK)
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ap.dbg) {
+        const dflash::ValidateArgs v =
+            c.plan.empty ? validate_args(page_table, ctx_lens, block_lens, nullptr, 0, 0, 1, true, desc,
+                                         const_cast<uint32_t*>(ap.dbg))
+                         : c.check;
+        const hipError_t ev = dflash::launch_validate(v, s);
+        if (ev != hipSuccess)
+            return fail(DFLASH_ERR_HIP, "debug-check kernel launch failed: %s", hipGetErrorString(ev));
+    }
     if (ap.total_rows > 0) {
         const hipError_t e = dflash::launch_kv_append(ap, s);
         if (e != hipSuccess)
@@ -545,7 +662,7 @@ int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new
     }
     if (c.plan.empty)
         return DFLASH_OK;
-    return attn_launch(c, desc, s);
+    return attn_launch(c, desc, s, /*validate=*/false);
 }
 
 }  // extern "C"

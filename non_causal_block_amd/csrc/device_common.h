@@ -206,6 +206,7 @@ struct AttnArgs {
     int32_t page_shift;
     int32_t max_pages_per_req;
     float scale_log2;  // scale * log2(e)
+    const uint32_t* dbg;  // debug-check state or nullptr: when it is non-zero the kernel does nothing
 };
 
 struct CombineArgs {
@@ -219,6 +220,7 @@ struct CombineArgs {
     int32_t D;
     int32_t Dp;
     int64_t total_rows;  // total_q hint * Hq
+    const uint32_t* dbg;  // as in AttnArgs
 };
 
 struct ConvArgs {
@@ -248,6 +250,27 @@ struct AppendArgs {
     int32_t page_shift;
     int32_t max_pages_per_req;
     int64_t total_rows;  // total_q * Hkv
+    const uint32_t* dbg;  // as in AttnArgs
+};
+
+// Debug checks of the device-side values a call relies on (debug_checks.hip).
+struct ValidateArgs {
+    const int32_t* page_table;
+    const int32_t* ctx_lens;
+    const int32_t* block_lens;
+    const int32_t* span_offsets;  // or nullptr
+    int32_t B;
+    int32_t page_size;
+    int32_t max_pages_per_req;
+    int32_t window;         // attention window (<= 0: none); sets the first page attention reads
+    int32_t tile_keys;      // key tile of the attention kernel (the first key read is a multiple)
+    int32_t from_block;     // 1: only the block's own positions are touched (append alone)
+    int64_t num_pages;
+    int64_t total_q;        // desc->total_q
+    int32_t max_block_len;  // hint (0 = none)
+    int32_t num_spans;
+    int64_t total_kv_len;   // hint (0 = none)
+    uint32_t* state;        // [0] sticky error bits, [1] lowest failing request
 };
 
 }  // namespace dflash

@@ -33,6 +33,10 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // DFlash2 in-block grouped dynamic depthwise convolution
 hipError_t launch_block_conv(const ConvArgs& a, hipStream_t stream);
 
+// debug checks: the per-device state word (static device memory) and the checking kernel
+hipError_t debug_state_ptr(uint32_t** out);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
+
 // streaming read of bytes (a multiple of 16) with grid workgroups, XOR of all words into *sink
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t stream);
 

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
 
@@ -43,6 +43,16 @@ def test_stream_read_rejects_bad_arguments(lib):
     assert nb.dflash_stream_read(0x1000, 15, 0x2000, None) == nb.DFLASH_ERR_INVALID_ARGUMENT
     assert nb.dflash_stream_read(0x1008, 16, 0x2000, None) == nb.DFLASH_ERR_INVALID_ARGUMENT
     assert nb.dflash_stream_read(0x1000, 0, 0x2000, None) == nb.DFLASH_OK  # nothing to read
+
+
+def test_debug_check_switch_and_argument_errors(lib):
+    prev = nb.dflash_set_debug_checks(True)
+    try:
+        assert nb.dflash_set_debug_checks(False) is True
+        assert nb.dflash_set_debug_checks(False) is False
+    finally:
+        nb.dflash_set_debug_checks(prev)
+    expect(lib.dflash_debug_checks_result(None, None), nb.DFLASH_ERR_INVALID_ARGUMENT, "non-NULL")
 
 
 def test_abi_version(lib):
