@@ -123,6 +123,8 @@ struct Plan {
     int row_tiles = 0;
     int Dp = 0;
     int combine_wgs = 0;
+    int combine_pps = 16;  // partial rows each combine lane requests together
+    int combine_lpr = 64;  // combine lanes per output row
     int ov = 0;
     size_t off_lse = 0;
     size_t ws_bytes = 0;
@@ -231,7 +233,16 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
         const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(uint16_t);  // bf16 partials
         p->off_lse = align_up(o_bytes);
         p->ws_bytes = p->off_lse + align_up((size_t)p->P * 2 * p->rmax * sizeof(float));
-        p->combine_wgs = dflash::combine_grid((int64_t)desc->total_q * Hq);
+        p->combine_lpr = kernel == DFLASH_KERNEL_MFMA ? dflash::combine_lanes_per_row(p->Dp, Hq) : 64;
+        p->combine_wgs = dflash::combine_grid((int64_t)desc->total_q * Hq, p->combine_lpr);
+        // Expected pieces per split unit: the runs over the units, plus the two that
+        // straddle each unit's ends.  Few pieces and many output rows want the lean
+        // combine (more resident waves); many pieces want all rows in one round.
+        int64_t units = (int64_t)desc->num_reqs * Hkv;
+        if (desc->max_block_len > 0)
+            units *= ((int64_t)desc->max_block_len * G + p->rmax - 1) / p->rmax;
+        const int64_t pieces = P / std::max<int64_t>(1, units) + 2;
+        p->combine_pps = pieces <= 4 ? 4 : pieces <= 8 ? 8 : 16;
     }
     return DFLASH_OK;
 }
@@ -375,7 +386,7 @@ int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t
         c.Dp = p.Dp;
         c.total_rows = (int64_t)desc->total_q * a.Hq;
         c.dbg = a.dbg;
-        e = dflash::launch_combine(c, p.combine_wgs, s);
+        e = dflash::launch_combine(c, p.combine_wgs, p.combine_pps, p.combine_lpr, s);
         if (e != hipSuccess)
             return fail(DFLASH_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
     }

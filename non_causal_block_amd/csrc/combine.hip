@@ -16,21 +16,31 @@
 
 namespace dflash {
 
-constexpr int kCombineRowsPerWg = 4;  // one wave each
-constexpr int kPiecesPerStep = 16;   // partial rows requested together by each lane
+constexpr int kCombineWavesPerWg = 4;
 
+// PPS: partial rows each lane requests together.  More rows in flight pay one latency
+// for a unit split many ways; fewer keep the registers low enough for many resident
+// waves when there are many rows and few pieces each.
+// LPR: lanes per output row (8 head-dim elements each): 64 / LPR rows share a wave,
+// so head_dim 128 or 256 does not leave most lanes idle.  All rows of a wave belong
+// to one token (the planner uses LPR < 64 only when Hq is a multiple of 64 / LPR).
+template <int PPS, int LPR>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 {
+    constexpr int RPW = 64 / LPR;
     if (a.dbg && *a.dbg != 0u)
         return;  // debug checks found a bad device-side value: touch nothing
     const Decomp& d = a.d;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kCombineRowsPerWg + wave;
-    if (row >= a.total_rows)
+    const int rg = lane / LPR;  // row of this lane within the wave
+    const int sl = lane % LPR;  // lane within the row's group
+    const int gbase = rg * LPR;
+    const int64_t row0 = ((int64_t)blockIdx.x * kCombineWavesPerWg + wave) * RPW;
+    if (row0 >= a.total_rows)
         return;
-    const int64_t t = row / a.Hq;
-    const int32_t h = (int32_t)(row % a.Hq);
+    const int64_t t = row0 / a.Hq;
+    const int32_t h = (int32_t)(row0 % a.Hq) + rg;
 
     int32_t r;
     int64_t qstart, rbase, total;
@@ -52,42 +62,55 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int64_t us = rbase + (int64_t)unit * g.uwork;
     int64_t kf, kl;
     unit_pieces(g, us, d.ov, tpw, kf, kl);
-    if (kf == kl)
-        return;  // finished inside one workgroup, already written
+    // a unit finished inside one workgroup is already written; its lanes only take
+    // part in the wave's shuffles
+    const bool split = kf != kl;
+    if (!__any(split))
+        return;
+    const int64_t npieces = split ? kl - kf + 1 : 0;
+    int64_t max_np = npieces;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        max_np = max(max_np, shfl_i64(max_np, lane ^ off));
 
-    // Lane j holds piece kf + j (+ 64 per round).  The log-sum-exps and the partial rows
-    // are requested together (rows of pieces that saw no key hold zeros, so they need no
-    // guard), and the weights are formed once everything has arrived.
-    const int64_t npieces = kl - kf + 1;
-    const int32_t d0 = lane * 8;
-    const bool dlive = d0 < a.D;
+    // Lane sl of a row's group holds piece kf + sl (+ LPR per round).  The
+    // log-sum-exps and the partial rows are requested together (rows of pieces that
+    // saw no key hold zeros, so they need no guard), and the weights are formed while
+    // the rows are in flight.
+    const int32_t d0 = sl * 8;
+    const bool dlive = split && d0 < a.D;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
         acc[e] = 0.f;
     float M = -INFINITY;
     float W = 0.f;
-    for (int64_t base = 0; base < npieces; base += 64) {
-        const int64_t kq = kf + base + lane;
-        const float lse = kq <= kl ? a.part_lse[(kq * 2 + piece_slot(kq, us, tpw)) * d.rmax + rin] : -INFINITY;
-        const int cnt = (int)min<int64_t>(64, npieces - base);
-        float wl = 0.f;
-        for (int j0 = 0; j0 < cnt; j0 += kPiecesPerStep) {
-            uint4 x[kPiecesPerStep];
+    for (int64_t base = 0; base < max_np; base += LPR) {
+        const int64_t kq = kf + base + sl;
+        const float lse = (split && base + sl < npieces)
+                              ? a.part_lse[(kq * 2 + piece_slot(kq, us, tpw)) * d.rmax + rin]
+                              : -INFINITY;
+        const int cnt = (int)max<int64_t>(0, min<int64_t>(LPR, npieces - base));
+        int max_cnt = cnt;
 #pragma unroll
-            for (int u = 0; u < kPiecesPerStep; ++u) {
-                const int jj = min(j0 + u, cnt - 1);
-                const int64_t k = kf + base + jj;
+        for (int off = 32; off >= 1; off >>= 1)
+            max_cnt = max(max_cnt, __shfl_xor(max_cnt, off));
+        float wl = 0.f;
+        for (int j0 = 0; j0 < max_cnt; j0 += PPS) {
+            uint4 x[PPS];
+#pragma unroll
+            for (int u = 0; u < PPS; ++u) {
+                const int64_t k = kf + base + j0 + u;
                 const int64_t prow = (k * 2 + piece_slot(k, us, tpw)) * d.rmax + rin;
                 x[u] = (dlive && j0 + u < cnt) ? *reinterpret_cast<const uint4*>(a.part_o + prow * a.Dp + d0)
                                                : make_uint4(0, 0, 0, 0);
             }
             if (j0 == 0) {
                 // weights of this round, formed while the rows above are in flight; what
-                // earlier rounds summed (more than 64 pieces only) is rescaled to the new max
+                // earlier rounds summed (more than LPR pieces only) is rescaled to the new max
                 float mr = lse;
 #pragma unroll
-                for (int off = 32; off >= 1; off >>= 1)
+                for (int off = LPR / 2; off >= 1; off >>= 1)
                     mr = fmaxf(mr, __shfl_xor(mr, off));
                 const float m_new = fmaxf(M, mr);
                 if (base > 0 && m_new > M) {
@@ -102,8 +125,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
                 W += wl;
             }
 #pragma unroll
-            for (int u = 0; u < kPiecesPerStep; ++u) {
-                const float wj = (j0 + u < cnt) ? __shfl(wl, min(j0 + u, cnt - 1)) : 0.f;
+            for (int u = 0; u < PPS; ++u) {
+                const int src = gbase + min(j0 + u, LPR - 1);
+                const float wsh = __shfl(wl, src);
+                const float wj = (j0 + u < cnt) ? wsh : 0.f;
                 const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -115,9 +140,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
         }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int off = LPR / 2; off >= 1; off >>= 1)
         W += __shfl_xor(W, off);
-    if (d0 < a.D) {
+    if (dlive) {
         const float inv = W > 0.f ? 1.f / W : 0.f;
         uint16_t* dst = a.out + (t * a.Hq + h) * (int64_t)a.D + d0;
         uint4 packed;
@@ -129,15 +154,38 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     }
 }
 
-int combine_grid(int64_t total_rows)
+int combine_lanes_per_row(int dpad, int32_t n_heads)
 {
-    return (int)((total_rows + kCombineRowsPerWg - 1) / kCombineRowsPerWg);
+    const int lpr = dpad <= 128 ? 16 : dpad <= 256 ? 32 : 64;
+    return n_heads % (64 / lpr) == 0 ? lpr : 64;
 }
 
-hipError_t launch_combine(const CombineArgs& a, int grid, hipStream_t stream)
+int combine_grid(int64_t total_rows, int lanes_per_row)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, a);
+    const int64_t rows_per_wg = (int64_t)kCombineWavesPerWg * (64 / lanes_per_row);
+    return (int)((total_rows + rows_per_wg - 1) / rows_per_wg);
+}
+
+template <int LPR>
+static hipError_t launch_lpr(const CombineArgs& a, int grid, int pps, hipStream_t stream)
+{
+    switch (pps) {
+    case 4: hipLaunchKernelGGL((combine_kernel<4, LPR>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((combine_kernel<8, LPR>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((combine_kernel<16, LPR>), dim3(grid), dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, int grid, int pieces_per_step, int lanes_per_row, hipStream_t stream)
+{
+    switch (lanes_per_row) {
+    case 16: return launch_lpr<16>(a, grid, pieces_per_step, stream);
+    case 32: return launch_lpr<32>(a, grid, pieces_per_step, stream);
+    case 64: return launch_lpr<64>(a, grid, pieces_per_step, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace dflash

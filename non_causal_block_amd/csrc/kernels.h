@@ -23,8 +23,11 @@ int mfma_max_row_tiles(int dpad);
 int mfma_wgs_per_cu(int dpad, int row_tiles, bool exact);  // on the current device (0 if unknown)
 
 // Split-KV combine.
-int combine_grid(int64_t total_rows);
-hipError_t launch_combine(const CombineArgs& a, int grid, hipStream_t stream);
+// lanes per output row (16, 32 or 64) for a padded head_dim and head count
+int combine_lanes_per_row(int dpad, int32_t n_heads);
+int combine_grid(int64_t total_rows, int lanes_per_row);
+// pieces_per_step 4, 8 or 16
+hipError_t launch_combine(const CombineArgs& a, int grid, int pieces_per_step, int lanes_per_row, hipStream_t stream);
 
 // block K/V rows -> their pages (one wave per (token, kv-head) row)
 int append_grid(int64_t total_rows);

@@ -107,6 +107,8 @@ EDGE = [
     (8, 2, 256, [333, 77], [9, 9], [0, 1], 40, 32),                # page size 32
     (8, 2, 128, [0], [1], [0], 0, 16),                             # a single key
     (12, 3, 128, [1000, 2, 515], [15, 16, 9], [1, 0, 1], 100, 16),
+    (6, 2, 128, [700, 33], [9, 5], [0, 1], 0, 16),                 # Hq not a multiple of the combine's rows per wave
+    (3, 3, 64, [400, 90], [7, 3], [1, 0], 0, 16),                  # Hq == Hkv == 3, head_dim 64
 ]
 
 
