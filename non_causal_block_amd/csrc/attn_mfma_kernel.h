@@ -222,21 +222,12 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     for (int s = 0; s < KS; ++s)
         dval[s] = EXACT || (wbase + 32 * s + 8 * grp4 < D);
 
-    const int64_t total = wave_total_work(a.ctx_lens, a.block_lens, d);
-    const int64_t tpw = tiles_per_wg(total, d.P);
-    const int64_t begin = (int64_t)wg * tpw;
-    const int64_t end = min(total, begin + tpw);
+    int64_t total, begin, end;
+    int32_t r_first = 0;
+    int64_t rbase_first = 0, qstart_first = 0;  // request of the run's first tile, its work and tokens before
+    wave_locate_run(a.ctx_lens, a.block_lens, d, wg, total, begin, end, r_first, rbase_first, qstart_first);
     if (begin >= end)
         return;
-
-    int32_t r_first;
-    int64_t rbase_first;
-    wave_find_request(a.ctx_lens, a.block_lens, d, begin, r_first, rbase_first);
-    int64_t qstart_first = 0;  // first query token of request r_first
-    for (int32_t base = 0; base < r_first; base += 64) {
-        int64_t nn = (base + lane < r_first) ? (int64_t)a.block_lens[base + lane] : 0;
-        qstart_first += shfl_i64(wave_inclusive_scan(nn), 63);
-    }
 
     // Segments of this workgroup's run that a lazy pass abandoned (bit i: i-th segment;
     // segments past 63 share the overflow flag and are all recomputed).

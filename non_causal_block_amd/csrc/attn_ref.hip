@@ -42,20 +42,12 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
     const int32_t G = d.G;
     const int32_t psize = 1 << a.page_shift;
 
-    const int64_t total = wave_total_work(a.ctx_lens, a.block_lens, d);
-    const int64_t tpw = tiles_per_wg(total, d.P);
-    const int64_t begin = (int64_t)wg * tpw;
-    const int64_t end = min(total, begin + tpw);
+    int64_t total, begin, end;
+    int32_t r = 0;
+    int64_t rbase = 0, qstart = 0;  // request of the run's first tile, its work and first query token
+    wave_locate_run(a.ctx_lens, a.block_lens, d, wg, total, begin, end, r, rbase, qstart);
     if (begin >= end)
         return;
-
-    int32_t r;
-    int64_t rbase;
-    wave_find_request(a.ctx_lens, a.block_lens, d, begin, r, rbase);
-    // first query token of request r
-    int64_t qstart = 0;
-    for (int32_t i = 0; i < r; ++i)
-        qstart += a.block_lens[i];
 
     int64_t pos = begin;
     int nseg = 0;

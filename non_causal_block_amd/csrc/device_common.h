@@ -136,6 +136,52 @@ __device__ __forceinline__ int64_t wave_work_before(const int32_t* __restrict__ 
     return acc;
 }
 
+// The run of workgroup wg: total work, its flat range [begin, end), and the request
+// holding `begin` with the work and query tokens before that request.  For up to 64
+// requests everything comes from one load of the length arrays (one memory round
+// trip before the first segment); larger batches take the general helpers.  When
+// begin >= end the request fields are not set.  Wave-uniform.
+__device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_lens,
+                                                const int32_t* __restrict__ block_lens, const Decomp& d, int32_t wg,
+                                                int64_t& total, int64_t& begin, int64_t& end, int32_t& r_out,
+                                                int64_t& rbase_out, int64_t& qstart_out)
+{
+    const int lane = threadIdx.x & 63;
+    if (d.B <= 64) {
+        const bool live = lane < d.B;
+        const int32_t L = live ? ctx_lens[lane] : 0;
+        const int32_t n = live ? block_lens[lane] : 0;
+        const int64_t w = live ? req_work(req_geom(L, n, d), d) : 0;
+        const int64_t wincl = wave_inclusive_scan(w);
+        const int64_t qincl = wave_inclusive_scan((int64_t)n);
+        total = shfl_i64(wincl, 63);
+        const int64_t tpw = tiles_per_wg(total, d.P);
+        begin = (int64_t)wg * tpw;
+        end = min(total, begin + tpw);
+        if (begin >= end)
+            return;
+        const unsigned long long m = __ballot(wincl > begin);
+        const int src = __ffsll((long long)m) - 1;
+        r_out = src;
+        rbase_out = shfl_i64(wincl - w, src);
+        qstart_out = shfl_i64(qincl - n, src);
+        return;
+    }
+    total = wave_total_work(ctx_lens, block_lens, d);
+    const int64_t tpw = tiles_per_wg(total, d.P);
+    begin = (int64_t)wg * tpw;
+    end = min(total, begin + tpw);
+    if (begin >= end)
+        return;
+    wave_find_request(ctx_lens, block_lens, d, begin, r_out, rbase_out);
+    int64_t q = 0;
+    for (int32_t base = 0; base < r_out; base += 64) {
+        const int64_t nn = (base + lane < r_out) ? (int64_t)block_lens[base + lane] : 0;
+        q += shfl_i64(wave_inclusive_scan(nn), 63);
+    }
+    qstart_out = q;
+}
+
 // One pass over the request arrays, 64 requests per step (one load round for up to
 // 64 requests): the request holding packed query token t with its first token, the
 // flat work before it, and the call's total work.  r_out = B for a token past the

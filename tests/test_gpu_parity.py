@@ -216,6 +216,22 @@ def test_split_invariance():
         assert float(np.max(diff)) <= 4e-3, (nwg, float(np.max(diff)))
 
 
+@pytest.mark.parametrize("kname,kernel", KERNELS)
+def test_more_than_64_requests(kname, kernel):
+    """130 requests: the kernels locate runs and tokens over several 64-request
+    chunks of the length arrays (the one-load path covers at most 64)."""
+    rng = np.random.default_rng(77)
+    B = 130
+    L = rng.integers(0, 400, size=B)
+    n = rng.integers(0, 10, size=B)
+    c = rng.integers(0, 2, size=B)
+    wl = workloads.build(B, 8, 2, 128, L, n, c, seed=78)
+    ref = oracle.run_workload(wl)
+    for nwg in (0, 37):
+        got = H.to_f64(H.run(wl, kernel=kernel, num_workgroups=nwg))
+        H.assert_parity(got, ref, f"B=130 kernel={kname} wg={nwg}")
+
+
 def test_combine_over_more_than_64_pieces():
     """A unit split over hundreds of workgroups: the combine merges its pieces in
     rounds of 64 (rescaling earlier rounds to the running maximum).  One long request
