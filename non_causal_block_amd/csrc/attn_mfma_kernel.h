@@ -665,7 +665,8 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 for (int r0 = wave * RPI; r0 < C::ROWS; r0 += WAVES * RPI) {
                     const int row = r0 + rsub;
                     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + row * C::SROW + ch * 16);
-                    *reinterpret_cast<u32x4_t*>(a.part_o + (sbase + row) * DP + ch * 8) = x;
+                    // streaming store: the combine reads the partial once, from HBM
+                    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(a.part_o + (sbase + row) * DP + ch * 8));
                 }
                 if (wave == 0 && grp4 == 0) {
 #pragma unroll
