@@ -223,9 +223,8 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
         dval[s] = EXACT || (wbase + 32 * s + 8 * grp4 < D);
 
     int64_t total, begin, end;
-    int32_t r_first = 0;
-    int64_t rbase_first = 0, qstart_first = 0;  // request of the run's first tile, its work and tokens before
-    wave_locate_run(a.ctx_lens, a.block_lens, d, wg, total, begin, end, r_first, rbase_first, qstart_first);
+    RunStart first;
+    wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first);
     if (begin >= end)
         return;
 
@@ -241,20 +240,25 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     // Walks the run; phase 0 runs every segment lazily, phase 1 recomputes abandoned ones.
     auto walk = [&](auto phase_tag) {
         constexpr int PHASE = decltype(phase_tag)::value;
-        int32_t r = r_first;
-        int64_t rbase = rbase_first;
-        int64_t qstart = qstart_first;
+        int32_t r = first.r;
+        int64_t rbase = first.rbase;
+        int64_t qstart = first.qstart;
+        // lengths and flag of request r (the first request's come with the run)
+        int32_t L = first.L, n = first.n;
+        bool is_causal = first.causal;
         int64_t pos = begin;
         int seg = 0;
         while (pos < end) {
-            const int32_t L = a.ctx_lens[r];
-            const int32_t n = a.block_lens[r];
             const ReqGeom g = req_geom(L, n, d);
             const int64_t w = req_work(g, d);
             if (pos >= rbase + w) {
+                // pos < end <= total work, so request r + 1 exists
                 rbase += w;
                 qstart += n;
                 ++r;
+                L = a.ctx_lens[r];
+                n = a.block_lens[r];
+                is_causal = a.causal ? (a.causal[r] != 0) : false;
                 continue;
             }
             const Segment sg = run_segment(g, rbase, pos, end, d.ov);
@@ -276,7 +280,6 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
             const int32_t grp = unit % g.ngroups;
             const int slot = (this_seg == 0) ? 0 : 1;
             const bool whole = (t0 == 0 && t1 == g.ntiles);
-            const bool is_causal = a.causal ? (a.causal[r] != 0) : false;
             const int32_t row0 = grp * d.rmax;
             const int32_t rows_here = min(d.rmax, n * G - row0);
             const int32_t T = g.T;

@@ -43,11 +43,12 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
     const int32_t psize = 1 << a.page_shift;
 
     int64_t total, begin, end;
-    int32_t r = 0;
-    int64_t rbase = 0, qstart = 0;  // request of the run's first tile, its work and first query token
-    wave_locate_run(a.ctx_lens, a.block_lens, d, wg, total, begin, end, r, rbase, qstart);
+    RunStart first;
+    wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first);
     if (begin >= end)
         return;
+    int32_t r = first.r;
+    int64_t rbase = first.rbase, qstart = first.qstart;  // its work and first query token
 
     int64_t pos = begin;
     int nseg = 0;

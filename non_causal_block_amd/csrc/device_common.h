@@ -136,21 +136,31 @@ __device__ __forceinline__ int64_t wave_work_before(const int32_t* __restrict__ 
     return acc;
 }
 
-// The run of workgroup wg: total work, its flat range [begin, end), and the request
-// holding `begin` with the work and query tokens before that request.  For up to 64
-// requests everything comes from one load of the length arrays (one memory round
-// trip before the first segment); larger batches take the general helpers.  When
-// begin >= end the request fields are not set.  Wave-uniform.
+// First request of a workgroup's run, with what the kernels need of it.
+struct RunStart {
+    int32_t r;       // request holding the run's first tile
+    int64_t rbase;   // flat work before request r
+    int64_t qstart;  // query tokens before request r
+    int32_t L, n;    // its lengths
+    bool causal;     // its causal flag (false without a flag array)
+};
+
+// The run of workgroup wg: total work, its flat range [begin, end), and its first
+// request.  For up to 64 requests everything, the causal flags included, comes from
+// one load of the request arrays (one memory round trip before the first segment);
+// larger batches take the general helpers.  When begin >= end `rs` is not set.
+// Wave-uniform.
 __device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_lens,
-                                                const int32_t* __restrict__ block_lens, const Decomp& d, int32_t wg,
-                                                int64_t& total, int64_t& begin, int64_t& end, int32_t& r_out,
-                                                int64_t& rbase_out, int64_t& qstart_out)
+                                                const int32_t* __restrict__ block_lens,
+                                                const uint8_t* __restrict__ causal, const Decomp& d, int32_t wg,
+                                                int64_t& total, int64_t& begin, int64_t& end, RunStart& rs)
 {
     const int lane = threadIdx.x & 63;
     if (d.B <= 64) {
         const bool live = lane < d.B;
         const int32_t L = live ? ctx_lens[lane] : 0;
         const int32_t n = live ? block_lens[lane] : 0;
+        const int32_t c = (live && causal) ? (int32_t)causal[lane] : 0;
         const int64_t w = live ? req_work(req_geom(L, n, d), d) : 0;
         const int64_t wincl = wave_inclusive_scan(w);
         const int64_t qincl = wave_inclusive_scan((int64_t)n);
@@ -162,9 +172,12 @@ __device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_
             return;
         const unsigned long long m = __ballot(wincl > begin);
         const int src = __ffsll((long long)m) - 1;
-        r_out = src;
-        rbase_out = shfl_i64(wincl - w, src);
-        qstart_out = shfl_i64(qincl - n, src);
+        rs.r = src;
+        rs.rbase = shfl_i64(wincl - w, src);
+        rs.qstart = shfl_i64(qincl - n, src);
+        rs.L = __shfl(L, src);
+        rs.n = __shfl(n, src);
+        rs.causal = __shfl(c, src) != 0;
         return;
     }
     total = wave_total_work(ctx_lens, block_lens, d);
@@ -173,13 +186,16 @@ __device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_
     end = min(total, begin + tpw);
     if (begin >= end)
         return;
-    wave_find_request(ctx_lens, block_lens, d, begin, r_out, rbase_out);
+    wave_find_request(ctx_lens, block_lens, d, begin, rs.r, rs.rbase);
     int64_t q = 0;
-    for (int32_t base = 0; base < r_out; base += 64) {
-        const int64_t nn = (base + lane < r_out) ? (int64_t)block_lens[base + lane] : 0;
+    for (int32_t base = 0; base < rs.r; base += 64) {
+        const int64_t nn = (base + lane < rs.r) ? (int64_t)block_lens[base + lane] : 0;
         q += shfl_i64(wave_inclusive_scan(nn), 63);
     }
-    qstart_out = q;
+    rs.qstart = q;
+    rs.L = ctx_lens[rs.r];
+    rs.n = block_lens[rs.r];
+    rs.causal = causal ? causal[rs.r] != 0 : false;
 }
 
 // One pass over the request arrays, 64 requests per step (one load round for up to
