@@ -123,6 +123,24 @@ def _pmc_means(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def gpu_info() -> dict:
+    """Device name, CU count and the clocks rocm-smi reports (None where unavailable)."""
+    import subprocess
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "cus": props.multi_processor_count, "sclk": None, "mclk": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        info["sclk"] = card.get("sclk clock speed:")
+        info["mclk"] = card.get("mclk clock speed:")
+    except Exception:  # rocm-smi absent or not permitted: leave the clocks unknown
+        pass
+    return info
+
+
 def summarize_pmc(fetch_csv: str, write_csv: str, config: str) -> dict:
     """HBM bytes per launch of the attention kernel from FETCH_SIZE / WRITE_SIZE runs.
 
@@ -460,6 +478,14 @@ def main(argv=None) -> int:
             "kernel_sha": khash,
         },
         "cpu_baseline": cpu,
+        "timing_us": {
+            "call": {"mean": float(call_ms.mean() * 1e3), "median": float(np.median(call_ms) * 1e3),
+                     "p10": float(np.percentile(call_ms, 10) * 1e3), "p90": float(np.percentile(call_ms, 90) * 1e3)},
+            "attention_kernel": {"mean": float(att_ms.mean() * 1e3), "median": float(np.median(att_ms) * 1e3),
+                                 "p10": float(np.percentile(att_ms, 10) * 1e3),
+                                 "p90": float(np.percentile(att_ms, 90) * 1e3)},
+        },
+        "gpu": gpu_info(),
     }
     print(json.dumps(line), flush=True)
     return 0
