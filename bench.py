@@ -124,21 +124,12 @@ def _pmc_means(path: str, counter: str) -> dict:
 
 
 def gpu_info() -> dict:
-    """Device name, CU count and the clocks rocm-smi reports (None where unavailable)."""
-    import subprocess
-
+    """Device name and CU count (no clocks: reading them would need a helper process,
+    which must not be started from a process that has initialised the GPU)."""
     import torch
 
     props = torch.cuda.get_device_properties(0)
-    info = {"name": props.name, "cus": props.multi_processor_count, "sclk": None, "mclk": None}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values()))
-        info["sclk"] = card.get("sclk clock speed:")
-        info["mclk"] = card.get("mclk clock speed:")
-    except Exception:  # rocm-smi absent or not permitted: leave the clocks unknown
-        pass
-    return info
+    return {"name": props.name, "cus": props.multi_processor_count}
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str, config: str) -> dict:
