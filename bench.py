@@ -330,6 +330,13 @@ def main(argv=None) -> int:
               "(the work shards by request / kv-head with no communication; see DESIGN.md)", file=sys.stderr)
         return 2
 
+    if not args.no_cpu_baseline and not (args.graph_latency or args.conv):
+        # compile the oracle (if stale) now: a compiler must not be started from this
+        # process once it has initialised the GPU
+        import oracle
+
+        oracle.build()
+
     import numpy as np
     import torch
 

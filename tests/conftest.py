@@ -9,3 +9,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def pytest_sessionstart(session):
+    """Compile the oracle (if its library is missing or stale) before any test touches
+    the GPU: a compiler started from a process that has initialised the GPU is a
+    program replacing itself in a GPU process, which must not happen."""
+    import oracle
+
+    oracle.build()
