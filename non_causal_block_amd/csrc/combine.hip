@@ -68,10 +68,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     if (!__any(split))
         return;
     const int64_t npieces = split ? kl - kf + 1 : 0;
+    // loop bounds common to the wave (one row per wave: already uniform)
     int64_t max_np = npieces;
+    if constexpr (RPW > 1) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        max_np = max(max_np, shfl_i64(max_np, lane ^ off));
+        for (int off = 32; off >= LPR; off >>= 1)
+            max_np = max(max_np, shfl_i64(max_np, lane ^ off));
+    }
 
     // Lane sl of a row's group holds piece kf + sl (+ LPR per round).  The
     // log-sum-exps and the partial rows are requested together (rows of pieces that
@@ -92,9 +95,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
                               : -INFINITY;
         const int cnt = (int)max<int64_t>(0, min<int64_t>(LPR, npieces - base));
         int max_cnt = cnt;
+        if constexpr (RPW > 1) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-            max_cnt = max(max_cnt, __shfl_xor(max_cnt, off));
+            for (int off = 32; off >= LPR; off >>= 1)
+                max_cnt = max(max_cnt, __shfl_xor(max_cnt, off));
+        }
         float wl = 0.f;
         for (int j0 = 0; j0 < max_cnt; j0 += PPS) {
             uint4 x[PPS];
