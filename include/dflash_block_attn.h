@@ -64,7 +64,8 @@ typedef struct {
     int32_t total_q;           /* >= sum(block_lens): rows of q and out                                 */
     int32_t max_block_len;     /* >= max(block_lens) (0 = unknown); picks the row tiling                 */
     int64_t total_kv_len;      /* >= sum(ctx_lens + block_lens) (0 = unknown); sizes the work split      */
-    int32_t page_size;         /* tokens per KV page, a power of two in [1, 1024] (16 is the tuned one)  */
+    int32_t page_size;         /* tokens per KV page, a power of two in [1, 1024] (16 is the tuned one); \
+                                  page_size * n_kv_heads * head_dim must be < 2^31 (else UNSUPPORTED)  */
     int32_t max_pages_per_req; /* row stride (entries) of page_table, >= 1                               */
     int64_t num_pages;         /* rows of k_pages / v_pages, >= 1                                        */
     int32_t kernel;            /* DFLASH_KERNEL_* (0 = auto)                                             */

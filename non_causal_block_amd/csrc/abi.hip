@@ -163,6 +163,10 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "max_pages_per_req %d must be >= 1", desc->max_pages_per_req);
     if (desc->num_pages < 1)
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_pages %lld must be >= 1", (long long)desc->num_pages);
+    // one page of one of k_pages / v_pages is addressed with 32-bit element offsets
+    if ((int64_t)desc->page_size * Hkv * D >= ((int64_t)1 << 31))
+        return fail(DFLASH_ERR_UNSUPPORTED, "page_size * n_kv_heads * head_dim = %lld elements per page; must be < 2^31",
+                    (long long)desc->page_size * Hkv * D);
     if (desc->kernel < DFLASH_KERNEL_AUTO || desc->kernel > DFLASH_KERNEL_MFMA)
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "unknown kernel selector %d", desc->kernel);
     if (desc->num_workgroups < 0 || desc->num_cus < 0)

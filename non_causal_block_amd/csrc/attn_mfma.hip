@@ -7,14 +7,16 @@ namespace dflash {
 
 hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream)
 {
+    if (a.page_shift < 4)
+        return launch_attn_mfma_small_pages(a, dpad, row_tiles, stream);
     if (a.span_offsets)
         return launch_attn_mfma_spans(a, dpad, row_tiles, stream);
-    return launch_dp<false>(a, dpad, row_tiles, stream);
+    return launch_dp<false, true>(a, dpad, row_tiles, stream);
 }
 
 // Resident workgroups per CU, queried once per kernel instance (the library runs on
-// one architecture, so the answer does not depend on the device).  The span
-// instances differ only in a few set-up instructions and share the plain ones'
+// one architecture, so the answer does not depend on the device).  The span and
+// small-page instances differ only in a few instructions and share the plain ones'
 // launch shape; the planner's count is an upper bound on workgroups in flight,
 // not something the kernel relies on.
 template <int DP, int RT, bool EXACT>
@@ -24,8 +26,8 @@ static int occupancy_one()
     int blocks = cached.load(std::memory_order_acquire);
     if (blocks >= 0)
         return blocks;
-    if (ensure_lds_limit<DP, RT, EXACT, false>() != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT, false>,
+    if (ensure_lds_limit<DP, RT, EXACT, false, true>() != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT, false, true>,
                                                      Cfg<DP, RT>::THREADS, Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
         return 0;
     cached.store(blocks, std::memory_order_release);

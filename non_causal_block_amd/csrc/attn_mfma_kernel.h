@@ -34,9 +34,9 @@
 //    workgroup recomputes such segments with each row's exact max found by a
 //    K-only pass.  Numerator and denominator share the reference, so the
 //    result is the same softmax either way.
-//  * Keys past the request's end are read from the request's first visible key
-//    row instead, so page-tail garbage (possibly NaN) is never loaded; their
-//    logits are masked, so their weight is exactly zero.
+//  * Keys past the request's end are read as its last key (T - 1) instead, so
+//    page-tail garbage (possibly NaN) is never loaded; their logits are masked,
+//    so their weight is exactly zero.
 //  * Epilogue: a unit finished inside the workgroup writes bf16 output;
 //    otherwise fp32 normalised partials + log2-sum-exp for combine.hip.
 #pragma once
@@ -176,7 +176,11 @@ struct Cfg {
 
 // EXACT: head_dim == DP, so every d-chunk exists and no lane needs masking.
 // SPANS: causal rows may be widened by bidirectional spans (a.span_offsets).
-template <int DP, int RT, bool EXACT, bool SPANS>
+// WIDEPG: pages hold at least 16 keys, so a 32-key tile lies in at most two pages
+// whose ids are wave-uniform.  (Smaller pages are a separate instance: a runtime
+// branch between the two ways of locating keys made the compiler wait for the
+// tile's LDS stores before every key address on the common path.)
+template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG>
 __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 {
     using C = Cfg<DP, RT>;
@@ -288,43 +292,48 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
             // address the row start instead (never past the row), and are zeroed
             const int64_t head_off = (int64_t)kvh * D;
 
-            // Element offset of the request's first visible key row: keys past the end (and
-            // tiles past the segment) read it, so every load stays in bounds and finite.
-            const int64_t safe_row =
-                ((int64_t)pt[g.kv_lo >> a.page_shift] * psize + (g.kv_lo & (psize - 1))) * d.Hkv * (int64_t)D;
             // Tile keys are located in two steps so that no wait lands on loads in flight:
             // tile_page() reads, one tile ahead, the page-table entry of key lane % 32 of the
-            // tile (at a clamped, always valid index); tile_rows() hands each lane the
+            // tile, clamped to the request's last key T - 1; tile_rows() hands each lane the
             // entries of its NI keys when the tile's K/V are requested -- two lane reads when
-            // a page spans 16 keys, else a shuffle per key.  Keys past the end and tiles
-            // past the segment get the safe row.
+            // a page holds at least 16 keys, else a shuffle per key.  Keys past the end read
+            // key T - 1 (a real key, so finite; its logit is masked), which keeps every load
+            // in bounds and away from page-tail garbage.
             auto tile_page = [&](int32_t t) -> int32_t {
                 const int32_t key = g.kv_lo + t * kTK + (lane & 31);
                 return pt[(key < T ? key : T - 1) >> a.page_shift];
             };
             const int32_t hkvd = d.Hkv * D;  // elements per key row
+            // element offset of this lane's 16 bytes inside a key row (< hkvd)
+            const int32_t lane_off = (int32_t)head_off + (lval ? wbase + 8 * sl : 0);
             auto tile_rows = [&](int32_t t, int32_t pgl, int64_t (&rows)[NI]) {
                 const int32_t k0 = g.kv_lo + t * kTK;
-                // keys at or past kend read the safe row (kend = 0 for a tile past the segment)
-                const int32_t kend = t < t1 ? T : 0;
-                int32_t page[NI];
-                if (a.page_shift >= 4) {
-                    const int32_t p0 = __builtin_amdgcn_readlane(pgl, 0);
-                    const int32_t p1 = __builtin_amdgcn_readlane(pgl, 16);
+                if constexpr (WIDEPG) {
+                    // Keys 0-15 of the tile lie in the page of its key 0, keys 16-31 in that
+                    // of its key 16 (tiles start at multiples of 32; a clamped key T - 1
+                    // lies in the page tile_page() read for its half).  A page's first
+                    // element comes from one wave-uniform product; a key adds its place in
+                    // the page, which fits 32 bits (page_size * Hkv * D < 2^31 is checked
+                    // on the host).
+                    const uint32_t p0 = (uint32_t)__builtin_amdgcn_readlane(pgl, 0);
+                    const uint32_t p1 = (uint32_t)__builtin_amdgcn_readlane(pgl, 16);
+                    const uint32_t page_elems = (uint32_t)psize * (uint32_t)hkvd;
+                    const int64_t base0 = (int64_t)((uint64_t)p0 * page_elems);
+                    const int64_t base1 = (int64_t)((uint64_t)p1 * page_elems);
 #pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        page[i] = (i * KPI) & 16 ? p1 : p0;
+                    for (int i = 0; i < NI; ++i) {
+                        const int32_t key = min(k0 + i * KPI + kl, T - 1);
+                        const uint32_t inpg = (uint32_t)(key & (psize - 1)) * (uint32_t)hkvd + (uint32_t)lane_off;
+                        rows[i] = (((i * KPI) & 16) ? base1 : base0) + inpg;
+                    }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < NI; ++i)
-                        page[i] = __builtin_amdgcn_ds_bpermute(4 * (i * KPI + kl), pgl);
-                }
-#pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    const int32_t key = k0 + i * KPI + kl;
-                    const uint64_t slot = (uint64_t)(uint32_t)page[i] * (uint32_t)psize + (uint32_t)(key & (psize - 1));
-                    const int64_t row = (int64_t)(slot * (uint32_t)hkvd);
-                    rows[i] = key < kend ? row : safe_row;
+                    for (int i = 0; i < NI; ++i) {
+                        const int32_t page = __builtin_amdgcn_ds_bpermute(4 * (i * KPI + kl), pgl);
+                        const int32_t key = min(k0 + i * KPI + kl, T - 1);
+                        const uint64_t slot = (uint64_t)(uint32_t)page * (uint32_t)psize + (uint32_t)(key & (psize - 1));
+                        rows[i] = (int64_t)(slot * (uint32_t)hkvd) + lane_off;
+                    }
                 }
             };
 
@@ -402,20 +411,19 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 }
                 bool aborted = false;
 
-                int64_t rows[NI];
+                int64_t rows[NI];  // element offsets of this lane's 16 bytes of each key it loads
                 int32_t pg_next;
                 u32x4_t kr[NI], vr[NI];
-                const int64_t lane_off = head_off + (lval ? wbase + 8 * sl : 0);
                 auto issue = [&](const uint16_t* base, u32x4_t (&dst)[NI]) {
 #pragma unroll
                     for (int i = 0; i < NI; ++i)
-                        dst[i] = ldg16_stream(base + rows[i] + lane_off);
+                        dst[i] = ldg16_stream(base + rows[i]);
                 };
 
                 // One 32-key tile per step.  At the top of step t the registers holding the
                 // K/V of tile t are written to LDS and at once refilled with tile t+1, which
                 // so has a whole step to arrive.  Inside the loop every request is
-                // unconditional (keys past the request read the safe row, page entries are
+                // unconditional (keys past the request read its last key, page entries are
                 // read at clamped indices): the loop has no divergent branches and each wait
                 // on the memory counter is exact.  The issue order (page entries, V, K) is pinned with
                 // scheduling barriers, here and in the loop: the compiler's waits at the
@@ -433,7 +441,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     constexpr bool PF = decltype(pf_tag)::value;
                     const int32_t k0 = g.kv_lo + t * kTK;
                     // (1) this wave's K and V slices -> LDS [key][d_local].  Keys past the
-                    // request hold the safe row and d past head_dim the row start: finite
+                    // request hold its last key and d past head_dim the row start: finite
                     // values whose weight (masked logit) or output column (never stored) is 0.
                     if constexpr (MODE != kMaxScan) {
 #pragma unroll
@@ -660,16 +668,20 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
             if (!whole) {
                 // A partial: bf16 rows of this workgroup's slot (a normalised partial is a
                 // convex combination of bf16 values, so bf16 holds its range; its rounding
-                // is that of the output itself).  Padding rows and head-dim columns past D
-                // land in the slot's own rows and row padding, which the combine never
-                // reads, so no store needs a predicate.
+                // is that of the output itself).  Head-dim columns past D land in the
+                // slot's row padding, which the combine never reads; padding rows are not
+                // stored at all (every workgroup writes its partial at about the same
+                // time, so these bytes are paid at the end of the kernel).
                 const int64_t sbase = ((int64_t)wg * 2 + slot) * d.rmax;
 #pragma unroll
                 for (int r0 = wave * RPI; r0 < C::ROWS; r0 += WAVES * RPI) {
                     const int row = r0 + rsub;
-                    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + row * C::SROW + ch * 16);
-                    // streaming store: the combine reads the partial once, from HBM
-                    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(a.part_o + (sbase + row) * DP + ch * 8));
+                    if (row < rows_here) {
+                        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + row * C::SROW + ch * 16);
+                        // streaming store: the combine reads the partial once, from HBM
+                        __builtin_nontemporal_store(x,
+                                                    reinterpret_cast<u32x4_t*>(a.part_o + (sbase + row) * DP + ch * 8));
+                    }
                 }
                 if (wave == 0 && grp4 == 0) {
 #pragma unroll
@@ -704,7 +716,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 
 // Raises a kernel's dynamic-LDS limit once per device (not on every launch: a call
 // being captured into a graph then enqueues nothing but the launch itself).
-template <int DP, int RT, bool EXACT, bool SPANS>
+template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG>
 static hipError_t ensure_lds_limit()
 {
     using C = Cfg<DP, RT>;
@@ -718,48 +730,48 @@ static hipError_t ensure_lds_limit()
     const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
     if (bit && (done.load(std::memory_order_acquire) & bit))
         return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel<DP, RT, EXACT, SPANS>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel<DP, RT, EXACT, SPANS, WIDEPG>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e == hipSuccess && bit)
         done.fetch_or(bit, std::memory_order_release);
     return e;
 }
 
-template <int DP, int RT, bool EXACT, bool SPANS>
+template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
 {
     using C = Cfg<DP, RT>;
-    const hipError_t e = ensure_lds_limit<DP, RT, EXACT, SPANS>();
+    const hipError_t e = ensure_lds_limit<DP, RT, EXACT, SPANS, WIDEPG>();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((attn_mfma_kernel<DP, RT, EXACT, SPANS>), dim3(a.d.P), dim3(C::THREADS), C::LDS_BYTES,
-                       stream, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<DP, RT, EXACT, SPANS, WIDEPG>), dim3(a.d.P), dim3(C::THREADS),
+                       C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
-template <int DP, bool EXACT, bool SPANS>
+template <int DP, bool EXACT, bool SPANS, bool WIDEPG>
 static hipError_t launch_rt(const AttnArgs& a, int row_tiles, hipStream_t stream)
 {
     switch (row_tiles) {
-    case 1: return launch_one<DP, 1, EXACT, SPANS>(a, stream);
-    case 2: return launch_one<DP, 2, EXACT, SPANS>(a, stream);
-    case 3: return launch_one<DP, 3, EXACT, SPANS>(a, stream);
-    case 4: return launch_one<DP, 4, EXACT, SPANS>(a, stream);
-    case 5: return launch_one<DP, 5, EXACT, SPANS>(a, stream);
+    case 1: return launch_one<DP, 1, EXACT, SPANS, WIDEPG>(a, stream);
+    case 2: return launch_one<DP, 2, EXACT, SPANS, WIDEPG>(a, stream);
+    case 3: return launch_one<DP, 3, EXACT, SPANS, WIDEPG>(a, stream);
+    case 4: return launch_one<DP, 4, EXACT, SPANS, WIDEPG>(a, stream);
+    case 5: return launch_one<DP, 5, EXACT, SPANS, WIDEPG>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <bool SPANS>
+template <bool SPANS, bool WIDEPG>
 static hipError_t launch_dp(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream)
 {
     switch (dpad) {
-    case 128: return a.D == 128 ? launch_rt<128, true, SPANS>(a, row_tiles, stream)
-                                : launch_rt<128, false, SPANS>(a, row_tiles, stream);
-    case 256: return a.D == 256 ? launch_rt<256, true, SPANS>(a, row_tiles, stream)
-                                : launch_rt<256, false, SPANS>(a, row_tiles, stream);
-    case 512: return a.D == 512 ? launch_rt<512, true, SPANS>(a, row_tiles, stream)
-                                : launch_rt<512, false, SPANS>(a, row_tiles, stream);
+    case 128: return a.D == 128 ? launch_rt<128, true, SPANS, WIDEPG>(a, row_tiles, stream)
+                                : launch_rt<128, false, SPANS, WIDEPG>(a, row_tiles, stream);
+    case 256: return a.D == 256 ? launch_rt<256, true, SPANS, WIDEPG>(a, row_tiles, stream)
+                                : launch_rt<256, false, SPANS, WIDEPG>(a, row_tiles, stream);
+    case 512: return a.D == 512 ? launch_rt<512, true, SPANS, WIDEPG>(a, row_tiles, stream)
+                                : launch_rt<512, false, SPANS, WIDEPG>(a, row_tiles, stream);
     default: return hipErrorInvalidValue;
     }
 }

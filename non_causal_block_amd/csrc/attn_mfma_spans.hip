@@ -8,7 +8,7 @@ namespace dflash {
 
 hipError_t launch_attn_mfma_spans(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream)
 {
-    return launch_dp<true>(a, dpad, row_tiles, stream);
+    return launch_dp<true, true>(a, dpad, row_tiles, stream);
 }
 
 }  // namespace dflash
