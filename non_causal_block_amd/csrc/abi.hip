@@ -125,6 +125,7 @@ struct Plan {
     int combine_wgs = 0;
     int combine_pps = 16;  // partial rows each combine lane requests together
     int combine_lpr = 64;  // combine lanes per output row
+    bool combine_rows = false;  // one output row per combine workgroup, pieces over its waves
     int ov = 0;
     size_t off_lse = 0;
     size_t ws_bytes = 0;
@@ -247,6 +248,13 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             units *= ((int64_t)desc->max_block_len * G + p->rmax - 1) / p->rmax;
         const int64_t pieces = P / std::max<int64_t>(1, units) + 2;
         p->combine_pps = pieces <= 4 ? 4 : pieces <= 8 ? 8 : 16;
+        // Units split more ways than one wave requests in one round (head_dim 512 at long
+        // contexts): a workgroup per output row, its four waves taking every fourth piece.
+        const int64_t rows = (int64_t)desc->total_q * Hq;
+        if (p->combine_lpr == 64 && pieces > 16 && rows <= 0x7fffffff) {
+            p->combine_rows = true;
+            p->combine_wgs = (int)rows;
+        }
     }
     return DFLASH_OK;
 }
@@ -390,7 +398,8 @@ int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t
         c.Dp = p.Dp;
         c.total_rows = (int64_t)desc->total_q * a.Hq;
         c.dbg = a.dbg;
-        e = dflash::launch_combine(c, p.combine_wgs, p.combine_pps, p.combine_lpr, s);
+        e = p.combine_rows ? dflash::launch_combine_rows(c, s)
+                           : dflash::launch_combine(c, p.combine_wgs, p.combine_pps, p.combine_lpr, s);
         if (e != hipSuccess)
             return fail(DFLASH_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
     }

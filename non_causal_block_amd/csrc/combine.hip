@@ -159,6 +159,155 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     }
 }
 
+// One output row per workgroup, its pieces dealt over the four waves (wave w takes
+// pieces w, w + 4, ...), for head_dim up to 512 (64 lanes x 8 elements).  A unit split
+// many ways (16 to 30 pieces at the long-context head_dim-512 shapes) then needs one
+// load round per wave instead of two for a single wave; the four partial sums, each
+// with its own running max, meet in LDS and wave 0 writes the row.
+template <int PPS>
+__global__ __launch_bounds__(256) void combine_row_kernel(CombineArgs a)
+{
+    constexpr int NW = kCombineWavesPerWg;
+    __shared__ float s_m[NW], s_w[NW];
+    __shared__ float s_acc[NW - 1][8][64];
+    if (a.dbg && *a.dbg != 0u)
+        return;  // debug checks found a bad device-side value: touch nothing
+    const Decomp& d = a.d;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = blockIdx.x;  // the grid has exactly total_rows workgroups
+    const int64_t t = row / a.Hq;
+    const int32_t h = (int32_t)(row % a.Hq);
+
+    int32_t r;
+    int64_t qstart, rbase, total;
+    wave_locate_token(a.ctx_lens, a.block_lens, d, t, r, qstart, rbase, total);
+    if (r >= d.B)
+        return;  // token past the real total (the same for every wave of the workgroup)
+    const int32_t L = a.ctx_lens[r];
+    const int32_t n = a.block_lens[r];
+    const ReqGeom g = req_geom(L, n, d);
+    const int64_t tpw = tiles_per_wg(total, d.P);
+    const int32_t rowreq = (int32_t)(t - qstart) * d.G + h % d.G;
+    const int32_t rin = rowreq % d.rmax;
+    const int32_t unit = (h / d.G) * g.ngroups + rowreq / d.rmax;
+    const int64_t us = rbase + (int64_t)unit * g.uwork;
+    int64_t kf, kl;
+    unit_pieces(g, us, d.ov, tpw, kf, kl);
+    if (kf == kl)
+        return;  // finished inside one attention workgroup: already written
+    const int64_t np = kl - kf + 1;
+    const int64_t cnt = np > wave ? (np - wave + NW - 1) / NW : 0;  // this wave's pieces
+    const int32_t d0 = lane * 8;
+    const bool dlive = d0 < a.D;
+    auto prow = [&](int64_t m) {  // partial row of the wave's m-th piece
+        const int64_t k = kf + wave + (int64_t)NW * m;
+        return (k * 2 + piece_slot(k, us, tpw)) * d.rmax + rin;
+    };
+
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.f;
+    float M = -INFINITY;
+    float W = 0.f;
+    for (int64_t base = 0; base < cnt; base += 64) {
+        const int64_t mq = base + lane;  // lane mq holds the log-sum-exp of piece mq
+        const float lse = mq < cnt ? a.part_lse[prow(mq)] : -INFINITY;
+        const int c = (int)min<int64_t>(64, cnt - base);
+        float wl = 0.f;
+        for (int j0 = 0; j0 < c; j0 += PPS) {
+            uint4 x[PPS];
+#pragma unroll
+            for (int u = 0; u < PPS; ++u)
+                x[u] = (dlive && j0 + u < c) ? *reinterpret_cast<const uint4*>(a.part_o + prow(base + j0 + u) * a.Dp + d0)
+                                             : make_uint4(0, 0, 0, 0);
+            if (j0 == 0) {
+                // weights of this round, formed while its rows are in flight; what earlier
+                // rounds summed (more than 64 pieces per wave only) moves to the new max
+                float mr = lse;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1)
+                    mr = fmaxf(mr, __shfl_xor(mr, off));
+                const float m_new = fmaxf(M, mr);
+                if (base > 0 && m_new > M) {
+                    const float sc = exp2f(M - m_new);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[e] *= sc;
+                    W *= sc;
+                }
+                M = m_new;
+                wl = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
+                W += wl;
+            }
+#pragma unroll
+            for (int u = 0; u < PPS; ++u) {
+                const float wsh = __shfl(wl, min(j0 + u, 63));
+                const float wj = (j0 + u < c) ? wsh : 0.f;
+                const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // bf16 -> fp32 is exact: the bits move to the high half
+                    acc[2 * e] = fmaf(wj, __uint_as_float(w4[e] << 16), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(wj, __uint_as_float(w4[e] & 0xffff0000u), acc[2 * e + 1]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        W += __shfl_xor(W, off);
+    if (lane == 0) {
+        s_m[wave] = M;  // -inf for a wave with no pieces (its W and acc are 0)
+        s_w[wave] = W;
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            s_acc[wave - 1][e][lane] = acc[e];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    // at least one piece saw a key (every query sees itself), so the common max is finite
+    float Mt = s_m[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+        Mt = fmaxf(Mt, s_m[w]);
+    const float sc0 = M == -INFINITY ? 0.f : exp2f(M - Mt);
+    float tot = sc0 * W;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] *= sc0;
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        const float sc = s_m[w] == -INFINITY ? 0.f : exp2f(s_m[w] - Mt);
+        tot = fmaf(sc, s_w[w], tot);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[e] = fmaf(sc, s_acc[w - 1][e][lane], acc[e]);
+    }
+    if (dlive) {
+        const float inv = tot > 0.f ? 1.f / tot : 0.f;
+        uint16_t* dst = a.out + (t * a.Hq + h) * (int64_t)a.D + d0;
+        uint4 packed;
+        packed.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
+        packed.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
+        packed.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
+        packed.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
+        *reinterpret_cast<uint4*>(dst) = packed;
+    }
+}
+
+hipError_t launch_combine_rows(const CombineArgs& a, hipStream_t stream)
+{
+    if (a.total_rows <= 0 || a.total_rows > 0x7fffffff || a.Dp > 512)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((combine_row_kernel<8>), dim3((unsigned)a.total_rows), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 int combine_lanes_per_row(int dpad, int32_t n_heads)
 {
     const int lpr = dpad <= 128 ? 16 : dpad <= 256 ? 32 : 64;

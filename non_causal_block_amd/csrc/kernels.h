@@ -30,6 +30,8 @@ int combine_lanes_per_row(int dpad, int32_t n_heads);
 int combine_grid(int64_t total_rows, int lanes_per_row);
 // pieces_per_step 4, 8 or 16
 hipError_t launch_combine(const CombineArgs& a, int grid, int pieces_per_step, int lanes_per_row, hipStream_t stream);
+// one output row per workgroup, pieces dealt over its four waves (head_dim <= 512); grid = total_rows
+hipError_t launch_combine_rows(const CombineArgs& a, hipStream_t stream);
 
 // block K/V rows -> their pages (one wave per (token, kv-head) row)
 int append_grid(int64_t total_rows);

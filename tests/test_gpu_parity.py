@@ -232,15 +232,18 @@ def test_more_than_64_requests(kname, kernel):
         H.assert_parity(got, ref, f"B=130 kernel={kname} wg={nwg}")
 
 
-def test_combine_over_more_than_64_pieces():
+@pytest.mark.parametrize("D,L0", [(128, 8000), (512, 12000)])
+def test_combine_over_more_than_64_pieces(D, L0):
     """A unit split over hundreds of workgroups: the combine merges its pieces in
     rounds of 64 (rescaling earlier rounds to the running maximum).  One long request
-    and one kv-head, so 600 workgroups take about one tile each."""
-    wl = workloads.build(2, 8, 1, 128, [8000, 300], [9, 5], [0, 1], seed=31)
+    and one kv-head, so 600 workgroups take about one tile each.  At head_dim 128 one
+    wave merges four rows; at head_dim 512 a workgroup merges one row with every
+    fourth piece per wave (375 pieces: more than 64 per wave)."""
+    wl = workloads.build(2, 8, 1, D, [L0, 300], [9, 5], [0, 1], seed=31)
     ref = oracle.run_workload(wl)
     for nwg in (150, 600):
         got = H.to_f64(H.run(wl, num_workgroups=nwg))
-        H.assert_parity(got, ref, f"many pieces wg={nwg}")
+        H.assert_parity(got, ref, f"many pieces D={D} wg={nwg}")
 
 
 def test_page_permutation_invariance_is_bitwise():
