@@ -425,7 +425,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 // so has a whole step to arrive.  Inside the loop every request is
                 // unconditional (keys past the request read its last key, page entries are
                 // read at clamped indices): the loop has no divergent branches and each wait
-                // on the memory counter is exact.  The issue order (page entries, V, K) is pinned with
+                // on the memory counter is exact.  The issue order (page entries, K, V) is pinned with
                 // scheduling barriers, here and in the loop: the compiler's waits at the
                 // loop head are exact only if both paths into it issue in the same order.
                 tile_rows(t0, pg_first, rows);
