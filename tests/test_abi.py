@@ -252,3 +252,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(OSError):
         _lib.load()
+
+
+def test_page_elements_limit(lib):
+    # a page of one of k_pages / v_pages is addressed with 32-bit element offsets: page_size *
+    # n_kv_heads * head_dim must stay below 2^31 (1024 * 4096 * 512 = 2^31 is refused)
+    d = desc(page_size=1024, max_pages_per_req=100)
+    expect(call(d, hq=4096, hkv=4096, hd=512), nb.DFLASH_ERR_UNSUPPORTED, "2^31")
+    # just below the limit the same shape is accepted by the planner
+    p = nb.dflash_block_attn_plan(desc(page_size=1024, max_pages_per_req=100), 4095, 4095, 512)
+    assert p.num_workgroups >= 1
