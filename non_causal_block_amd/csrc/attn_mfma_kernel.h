@@ -199,7 +199,12 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     float* mref_s = reinterpret_cast<float*>(lds + C::OFF_MREF);
     int* flag_s = reinterpret_cast<int*>(lds + C::OFF_FLAG);
 
-    const Decomp& d = a.d;
+    // The tile size and the rows per unit are fixed by the instance (the planner sets the
+    // same values); as constants, the work-split arithmetic divides by them with shifts and
+    // multiplications instead of division sequences.
+    Decomp d = a.d;
+    d.tk = kTK;
+    d.rmax = C::ROWS;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15;
