@@ -9,8 +9,10 @@
 // with pieces that saw no visible key (lse = -inf) weighing zero.  The
 // FlashAttention split-KV combine is the prior art named in vLLM PR #52816's
 // review (prhub summary, "review highlights"); this one is written for the
-// 9..72 query rows and head_dim up to 512 of a DFlash step: one wave per
-// output row, 8 consecutive head-dim elements per lane.
+// 9..72 query rows and head_dim up to 512 of a DFlash step, 8 consecutive
+// head-dim elements per lane.  combine_kernel gives an output row 16, 32 or 64
+// lanes of a wave; combine_row_kernel gives a row a whole workgroup, its four
+// waves taking every fourth piece, for units split many ways at head_dim 512.
 #include "device_common.h"
 #include "kernels.h"
 
