@@ -21,13 +21,16 @@
  *       keys ending at the query's position (the window bounds only the low
  *       side; for a non-causal request the high end stays T-1).
  *
- *   Bidirectional spans (optional; the mm-prefix case of the same notes,
- *   section "what MooreThreads/vllm-musa PR #52 did": a multimodal prefix is
- *   seen as a whole while text stays causal): request r lists spans
- *   [s, e) of key positions (span_offsets[r] .. span_offsets[r+1]-1 in
- *   `spans`, sorted, disjoint).  A query of a causal request whose position p
- *   lies in a span [s, e) also sees the keys of that span after it: the high
- *   end becomes max(p, e-1).  Non-causal requests see every key anyway.
+ *   Bidirectional spans (optional).  The same notes, section "what
+ *   MooreThreads/vllm-musa PR #52 did", only name an mm-prefix capability of
+ *   the backend; the rule below is this project's reading of it (the plainest
+ *   mask in which a multimodal prefix is seen as a whole while text stays
+ *   causal): request r lists spans [s, e) of key positions (span_offsets[r] ..
+ *   span_offsets[r+1]-1 in `spans`, any order, may overlap).  A query of a
+ *   causal request whose position p lies in a span [s, e) also sees the keys of
+ *   that span after it: the high end becomes max(p, e-1) over those spans, and
+ *   never passes the request's last key T-1 (a query sees only its own
+ *   request's keys).  Non-causal requests see every key anyway.
  *
  *   For q-head h, the kv-head is g = h / (Hq/Hkv) (contiguous GQA groups).
  *   z_j = scale * sum_d q[i,h,d] k[j,g,d]       (d ascending)
@@ -93,6 +96,8 @@ static void attend_one(const job_t *J, int64_t tok, int32_t h, double *o, double
             if (s <= p && p < e && e - 1 > hi)
                 hi = e - 1;
         }
+        if (hi > T - 1)
+            hi = T - 1;
     }
     int64_t lo = 0;
     if (J->window > 0) {

@@ -18,3 +18,18 @@ def pytest_sessionstart(session):
     import oracle
 
     oracle.build()
+
+
+def pytest_collection_finish(session):
+    """Compile the host programs the selected CPU tests run (decomposition checker,
+    oracle mutants, sanitizer builds) now, before any test -- and so before any GPU
+    test -- has run."""
+    from tests import native_builds
+
+    native_builds.prepare({item.module.__name__ for item in session.items if hasattr(item, "module")})
+
+
+def pytest_sessionfinish(session, exitstatus):
+    from tests import native_builds
+
+    native_builds.cleanup()

@@ -7,7 +7,9 @@
 //   * a unit handled whole by one workgroup is not also split,
 //   * the pieces of a split unit are exactly the (workgroup, slot) pairs the
 //     combine kernel derives from the unit's own tile range,
-//   * no slot of a workgroup is written twice.
+//   * no slot of a workgroup is written twice,
+//   * no two split units share their first workgroup (the in-kernel merge names a
+//     unit's counters by it) and that workgroup exists.
 // Prints "OK <units> <split units> <max pieces>" or "FAIL <reason>".
 #include <cstdio>
 #include <cstdlib>
@@ -106,6 +108,7 @@ int main()
     }
     int split = 0;
     size_t max_pieces = 0;
+    std::set<int64_t> first_wgs;
     for (int r = 0; r < d.B; ++r) {
         ReqGeom g = req_geom(L[r], n[r], d);
         for (int kvh = 0; kvh < (g.ngroups ? d.Hkv : 0); ++kvh)
@@ -124,6 +127,10 @@ int main()
                 }
                 ++split;
                 max_pieces = std::max(max_pieces, pl.size());
+                if (kf < 0 || kf >= d.P || !first_wgs.insert(kf).second) {
+                    printf("FAIL split units share their first workgroup %lld\n", (long long)kf);
+                    return 1;
+                }
                 if ((int64_t)pl.size() != kl - kf + 1) {
                     printf("FAIL split unit piece count\n");
                     return 1;

@@ -1,23 +1,18 @@
 """The work split shared by the planner, the attention kernels and the combine
 (non_causal_block_amd/csrc/decomp.h), checked on the host with g++."""
-import os
 import subprocess
 
 import numpy as np
 import pytest
 
 import workloads
-
-HERE = os.path.dirname(os.path.abspath(__file__))
-CSRC = os.path.join(os.path.dirname(HERE), "non_causal_block_amd", "csrc")
+from tests import native_builds
 
 
 @pytest.fixture(scope="module")
-def checker(tmp_path_factory):
-    exe = str(tmp_path_factory.mktemp("decomp") / "decomp_check")
-    subprocess.check_call(["g++", "-O2", "-std=c++17", "-I", CSRC, os.path.join(HERE, "host", "decomp_check.cpp"),
-                           "-o", exe])
-    return exe
+def checker():
+    # compiled at session start (tests/native_builds.py), never from a test body
+    return native_builds.get("decomp_check")
 
 
 def run(exe, L, n, Hkv, G, window, rmax, tk, P, ov=0):

@@ -1,19 +1,15 @@
 """The oracle's pins catch plausible mistakes.
 
 Each case plants one mistake in a private copy of oracle/oracle_f64.c (on the
-CPU, never on a GPU), builds it, and requires that at least one pin from
+CPU, never on a GPU; built at session start by tests/native_builds.py) and requires that at least one pin from
 tests/oracle_pins.py fails against the broken build while all pass against
 the real one.
 """
-import os
-import subprocess
-
 import pytest
 
 import oracle
+from tests import native_builds
 from tests import oracle_pins as pins
-
-SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle_f64.c")
 
 MUTANTS = {
     "window_off_by_one": ("lo = p - (int64_t)J->window + 1;", "lo = p - (int64_t)J->window;"),
@@ -42,13 +38,7 @@ def _any_pin_fails(lib) -> bool:
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
-    mpath = tmp_path / "mutant.c"
-    mpath.write_text(src.replace(old, new))
-    so = tmp_path / "libmutant.so"
-    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fPIC", "-shared", "-pthread", str(mpath),
-                           "-o", str(so), "-lm"])
-    assert _any_pin_fails(oracle.bind(str(so))), f"no pin caught the planted mistake {name}"
+def test_mutant_is_caught(name):
+    # the mutant libraries were compiled at session start (tests/native_builds.py)
+    so = native_builds.get("mutants")[name]
+    assert _any_pin_fails(oracle.bind(so)), f"no pin caught the planted mistake {name}"

@@ -106,3 +106,18 @@ def test_spans_do_not_touch_non_causal_requests_and_single_positions_do_nothing(
     base = oracle.block_attn_f64(q, k, v, ctx, blk, c, Hq, Hkv, D, 5, 0.3)
     spans = [[(21, 29)], [(7, 8), (9, 10), (11, 12)], [(13, 29)]]  # request 1: one-position spans only
     assert np.array_equal(oracle.block_attn_f64(q, k, v, ctx, blk, c, Hq, Hkv, D, 5, 0.3, spans=spans), base)
+
+
+def test_a_span_past_the_request_end_is_clipped_to_its_keys():
+    """A span may end past the request's last key T-1 (the ABI clips it); a query
+    sees only its own request's keys, so such a span equals the one cut at T, and
+    both equal the brute force (which only ever looks at keys 0..T-1)."""
+    ctx, blk, Hq, Hkv, D, q, k, v = _case()
+    c = np.ones(3, dtype=np.uint8)
+    T = ctx + blk
+    past = [[(int(ctx[0]) + 2, int(T[0]) + 50)], [(int(ctx[1]), int(T[1]) + 1)], [(0, int(T[2]) + 1000)]]
+    cut = [[(s, min(e, int(T[r]))) for s, e in sp] for r, sp in enumerate(past)]
+    a = oracle.block_attn_f64(q, k, v, ctx, blk, c, Hq, Hkv, D, 0, 0.3, spans=past)
+    assert np.array_equal(a, oracle.block_attn_f64(q, k, v, ctx, blk, c, Hq, Hkv, D, 0, 0.3, spans=cut))
+    b = brute.block_attn(_f(q), _f(k), _f(v), ctx, blk, c, Hq, Hkv, D, 0, 0.3, spans=past)
+    assert np.abs(a - b).max() <= 1e-12
