@@ -53,7 +53,7 @@ METRIC = "query-tokens/s + K/V HBM GB/s (% of peak) for block attention, 1 MI355
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_mfma_c3_global_d512.json")
 FLUSH_BYTES = 1 << 30
-KERNEL_SOURCES = ["attn_mfma_kernel.h", "attn_mfma.hip", "device_common.h", "decomp.h"]
+KERNEL_SOURCES = ["attn_mfma_kernel.h", "attn_mfma.hip", "device_common.h", "decomp.h", "merge.h"]
 
 
 def kernel_source_hash() -> str:
@@ -211,7 +211,7 @@ def graph_latency(reps: int = 200) -> dict:
             desc = nb.make_desc(num_reqs=B, total_q=wl.total_q, max_block_len=9, total_kv_len=wl.total_kv,
                                 page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req,
                                 num_pages=wl.num_pages)
-            ws = torch.empty(max(nb.dflash_block_attn_workspace_size(desc, wl.Hq, wl.Hkv, wl.D), 256),
+            ws = torch.zeros(max(nb.dflash_block_attn_workspace_size(desc, wl.Hq, wl.Hkv, wl.D), 256),
                              dtype=torch.uint8, device=dev)
             desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
             plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
@@ -315,6 +315,8 @@ def main(argv=None) -> int:
     ap.add_argument("--kernel", choices=["auto", "mfma", "ref"], default="auto")
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--merge", choices=["auto", "combine", "in-kernel"], default="auto",
+                    help="how split-KV pieces are merged (desc->merge_mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--graph-latency", action="store_true")
@@ -376,9 +378,11 @@ def main(argv=None) -> int:
     out = torch.empty((wl.total_q, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
     desc = nb.make_desc(num_reqs=wl.B, total_q=wl.total_q, max_block_len=int(wl.block_lens.max()),
                         total_kv_len=wl.total_kv, page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req,
-                        num_pages=wl.num_pages, kernel=kernel, num_workgroups=args.num_workgroups)
+                        num_pages=wl.num_pages, kernel=kernel, num_workgroups=args.num_workgroups,
+                        merge_mode={"auto": nb.DFLASH_MERGE_AUTO, "combine": nb.DFLASH_MERGE_COMBINE_KERNEL,
+                                    "in-kernel": nb.DFLASH_MERGE_IN_KERNEL}[args.merge])
     plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     flush.fill_(1.0)  # also the known-size write the WRITE_SIZE counter is calibrated with
@@ -418,7 +422,8 @@ def main(argv=None) -> int:
             raise nb.DFlashError(st, nb.dflash_last_error_message())
 
     print(f"[bench] plan: kernel={plan.kernel} workgroups={plan.num_workgroups} rows/unit={plan.rows_per_unit} "
-          f"combine={plan.combine_workgroups} workspace={plan.workspace_bytes}", file=sys.stderr, flush=True)
+          f"merge_in_kernel={plan.merge_in_kernel} combine={plan.combine_workgroups} "
+          f"workspace={plan.workspace_bytes}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i, False)
         step(i, True)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define DFLASH_ABI_VERSION 1
+#define DFLASH_ABI_VERSION 2
 
 /* Return codes. */
 typedef enum {
@@ -46,6 +46,13 @@ typedef enum {
     DFLASH_ERR_WORKSPACE_TOO_SMALL = 3,/* desc->workspace_bytes below dflash_block_attn_workspace_size */
     DFLASH_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
 } dflash_status;
+
+/* Merge of split-KV pieces (desc->merge_mode).  AUTO merges inside the attention kernel for
+   small grids (at most 64 workgroups: a launch-bound draft step, where a second kernel is a
+   large part of the call) and with the combine kernel otherwise (measured faster there). */
+#define DFLASH_MERGE_AUTO 0
+#define DFLASH_MERGE_COMBINE_KERNEL 1
+#define DFLASH_MERGE_IN_KERNEL 2
 
 /* Kernel selection (desc->kernel). */
 #define DFLASH_KERNEL_AUTO 0       /* the MFMA kernel where it applies, else the reference kernel */
@@ -71,10 +78,15 @@ typedef struct {
     int32_t kernel;            /* DFLASH_KERNEL_* (0 = auto)                                             */
     int32_t num_workgroups;    /* 0 = planner decides; >= 1 forces the attention grid (tests)            */
     int32_t num_cus;           /* 0 = query the current device; > 0 plans for that many compute units    */
-    void*   workspace;         /* device scratch owned by the caller, 256-byte aligned                    */
+    void*   workspace;         /* device scratch owned by the caller, 256-byte aligned, zero-filled     \
+                                  once before its first use (see below)                                  */
     size_t  workspace_bytes;   /* its size; must be >= dflash_block_attn_workspace_size(...)             */
     void*   event_attn_begin;  /* optional hipEvent_t recorded on `stream` right before the attention   */
     void*   event_attn_end;    /*   kernel and right after it (not around the combine); NULL = none     */
+    int32_t merge_mode;        /* how split-KV pieces are merged: DFLASH_MERGE_AUTO (0, the planner     \
+                                  picks), DFLASH_MERGE_COMBINE_KERNEL (1, a second kernel) or          \
+                                  DFLASH_MERGE_IN_KERNEL (2, the MFMA attention kernel itself; the      \
+                                  reference kernel always uses the combine kernel)                       */
 } dflash_batch_desc;
 
 /* What the planner decided for a call (dflash_block_attn_plan). */
@@ -84,7 +96,8 @@ typedef struct {
     int32_t tile_keys;         /* keys per tile                                                         */
     int32_t rows_per_unit;     /* query rows (block query x q-head of one kv-head) handled together    */
     int32_t head_dim_padded;   /* head_dim rounded up to the kernel's instantiation                      */
-    int32_t combine_workgroups;/* grid of the split-KV combine (0 = not launched)                        */
+    int32_t combine_workgroups;/* grid of the split-KV combine kernel (0 = not launched)                 */
+    int32_t merge_in_kernel;   /* 1: split-KV pieces are merged inside the attention kernel             */
     size_t  workspace_bytes;   /* scratch the call needs                                                */
 } dflash_plan_info;
 
@@ -110,14 +123,23 @@ typedef struct {
  *
  * Output rows are rounded to bf16 with round-to-nearest-even from fp32 accumulation.  When a
  * request's keys are split over several workgroups, each piece's normalised output is kept in
- * bf16 in the workspace (with an fp32 log-sum-exp) and the pieces are merged in fp32.
- * The call is asynchronous: it validates, enqueues one attention kernel and, when
- * some request's keys were split over several workgroups, one combine kernel, and
- * returns.  Buffers must stay valid until the stream has run the work.  Concurrent
- * calls need distinct workspaces.  On a non-OK return from validation nothing is
- * enqueued and `out` is untouched.  Device-side values outside the stated ranges
- * (negative lengths, page ids >= num_pages, L+n beyond max_pages_per_req*page_size)
- * are undefined behaviour.
+ * bf16 in the workspace (with an fp32 log-sum-exp) and the pieces are merged in fp32 (softmax
+ * over a union of disjoint key sets).
+ *
+ * The call is asynchronous: it validates, enqueues one attention kernel -- which, for small grids
+ * or when desc->merge_mode asks for it, also merges the split pieces -- or the attention kernel
+ * followed by a combine kernel, and returns.  Buffers must stay valid until the stream has run the work.
+ *
+ * Workspace: the caller allocates dflash_block_attn_workspace_size bytes and zero-fills them
+ * once (hipMemset, torch.zeros) before the first call that uses them.  The merge keeps
+ * counters at the start of the workspace; every call leaves them zero again when it has run,
+ * so no call needs a memset (graph capture).  After a call that did not run to completion
+ * (a launch failure, a device fault) zero-fill it again.  Calls that may run at the same time
+ * (different streams) need distinct workspaces.
+ *
+ * On a non-OK return from validation nothing is enqueued and `out` is untouched.
+ * Device-side values outside the stated ranges (negative lengths, page ids >= num_pages,
+ * L+n beyond max_pages_per_req*page_size) are undefined behaviour.
  */
 int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
                       const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads, int32_t n_kv_heads,
@@ -125,10 +147,12 @@ int dflash_block_attn(const void* q, const void* k_pages, const void* v_pages, c
                       void* stream, const dflash_batch_desc* desc);
 
 /*
- * dflash_block_attn with bidirectional spans inside causal requests: the
- * multimodal-prefix mask (kenforever1 "DFlash + Gemma 4 31B-it" notes, section
- * on MooreThreads/vllm-musa PR #52: an image prefix is attended as a whole while
- * text stays causal).  A query at position p of a causal request that lies in
+ * dflash_block_attn with bidirectional spans inside causal requests, for a
+ * multimodal prefix.  kenforever1 "DFlash + Gemma 4 31B-it" notes, section on
+ * MooreThreads/vllm-musa PR #52, only name the backend's mm-prefix support and
+ * warn that arbitrary partial 2D masks are not fully covered; the rule below is
+ * this library's reading (the plainest mask in which an image prefix is attended
+ * as a whole while text stays causal).  A query at position p of a causal request that lies in
  * one of the request's spans [s, e) also sees the keys after it up to e - 1:
  * its visible range becomes [lo, max(p, e - 1)] (lo from the window as before).
  * Positions count keys of the request from 0 (context 0..L-1, block L..L+n-1).

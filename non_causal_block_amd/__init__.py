@@ -21,7 +21,8 @@ from typing import Optional
 from . import _lib
 from ._lib import (DFLASH_ERR_HIP, DFLASH_ERR_INVALID_ARGUMENT, DFLASH_ERR_UNSUPPORTED,  # noqa: F401
                    DFLASH_ERR_WORKSPACE_TOO_SMALL, DFLASH_KERNEL_AUTO, DFLASH_KERNEL_MFMA, DFLASH_KERNEL_REFERENCE,
-                   DFLASH_OK, dflash_batch_desc, dflash_plan_info)
+                   DFLASH_MERGE_AUTO, DFLASH_MERGE_COMBINE_KERNEL, DFLASH_MERGE_IN_KERNEL, DFLASH_OK,
+                   dflash_batch_desc, dflash_plan_info)
 
 
 class DFlashError(RuntimeError):
@@ -164,7 +165,7 @@ def dflash_block_attn_append(q, k_new, v_new, k_pages, v_pages, page_table, ctx_
 # ---- convenience -------------------------------------------------------------
 def make_desc(*, num_reqs: int, total_q: int, max_block_len: int, total_kv_len: int, page_size: int,
               max_pages_per_req: int, num_pages: int, kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0,
-              num_cus: int = 0) -> dflash_batch_desc:
+              num_cus: int = 0, merge_mode: int = DFLASH_MERGE_AUTO) -> dflash_batch_desc:
     d = dflash_batch_desc()
     d.num_reqs = num_reqs
     d.total_q = total_q
@@ -176,13 +177,14 @@ def make_desc(*, num_reqs: int, total_q: int, max_block_len: int, total_kv_len: 
     d.kernel = kernel
     d.num_workgroups = num_workgroups
     d.num_cus = num_cus
+    d.merge_mode = merge_mode
     return d
 
 
 def block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, *, causal=None, window: int = 0,
                scale: Optional[float] = None, out=None, max_block_len: int = 0, total_kv_len: int = 0,
                kernel: int = DFLASH_KERNEL_AUTO, num_workgroups: int = 0, workspace=None, span_offsets=None,
-               spans=None):
+               spans=None, merge_mode: int = DFLASH_MERGE_AUTO):
     """Block attention on torch device tensors; returns ``out`` (bf16 [total_q, Hq, D]).
 
     q: bf16 [total_q, Hq, D]; k_pages/v_pages: bf16 [num_pages, page_size, Hkv, D];
@@ -190,7 +192,8 @@ def block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, *, causal=
     causal: uint8 [B] or None.  ``max_block_len``/``total_kv_len`` are host hints
     (0 = unknown).  ``span_offsets`` (int32 [B+1]) with ``spans`` (int32 [S, 2])
     add bidirectional spans to causal requests (dflash_block_attn_spans).  Runs on
-    torch's current stream.
+    torch's current stream.  A caller-given ``workspace`` (uint8 device tensor) must
+    have been zero-filled once before its first use; one allocated here is.
     """
     import torch
 
@@ -201,13 +204,13 @@ def block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, *, causal=
     B = ctx_lens.shape[0]
     desc = make_desc(num_reqs=B, total_q=total_q, max_block_len=max_block_len, total_kv_len=total_kv_len,
                      page_size=page_size, max_pages_per_req=page_table.shape[1], num_pages=num_pages,
-                     kernel=kernel, num_workgroups=num_workgroups)
+                     kernel=kernel, num_workgroups=num_workgroups, merge_mode=merge_mode)
     if out is None:
         out = torch.empty((total_q, Hq, D), dtype=torch.bfloat16, device=q.device)
     need = dflash_block_attn_workspace_size(desc, Hq, Hkv, D)
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         desc.workspace = workspace.data_ptr()
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if scale is None:

@@ -18,6 +18,10 @@ DFLASH_ERR_UNSUPPORTED = 2
 DFLASH_ERR_WORKSPACE_TOO_SMALL = 3
 DFLASH_ERR_HIP = 4
 
+DFLASH_MERGE_AUTO = 0
+DFLASH_MERGE_COMBINE_KERNEL = 1
+DFLASH_MERGE_IN_KERNEL = 2
+
 DFLASH_KERNEL_AUTO = 0
 DFLASH_KERNEL_REFERENCE = 1
 DFLASH_KERNEL_MFMA = 2
@@ -39,6 +43,7 @@ class dflash_batch_desc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("event_attn_begin", ctypes.c_void_p),
         ("event_attn_end", ctypes.c_void_p),
+        ("merge_mode", ctypes.c_int32),
     ]
 
 
@@ -50,6 +55,7 @@ class dflash_plan_info(ctypes.Structure):
         ("rows_per_unit", ctypes.c_int32),
         ("head_dim_padded", ctypes.c_int32),
         ("combine_workgroups", ctypes.c_int32),
+        ("merge_in_kernel", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

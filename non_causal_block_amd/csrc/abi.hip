@@ -19,6 +19,7 @@
 #include "dflash_block_attn.h"
 #include "decomp.h"
 #include "kernels.h"
+#include "merge.h"
 
 namespace {
 
@@ -116,6 +117,11 @@ constexpr int kSegmentCharge = 3;
 constexpr int kSegmentChargeShort = 2;
 constexpr int kChargeMinTiles = 16;
 constexpr size_t kAlign = 256;
+// Largest grid the automatic choice merges split units in: a small draft step is launch
+// bound, and merging in the attention kernel saves the second launch (C1's step: 18.4 ->
+// 16.7 us per call); larger grids pay more for the in-kernel merge's coherent publish and
+// waits than for a second kernel (C2 48.7 vs 60.0 us, C3 138.7 vs 147.4 us; A/B on one box).
+constexpr int kMergeInKernelAutoWgs = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -130,7 +136,10 @@ struct Plan {
     int combine_pps = 16;  // partial rows each combine lane requests together
     int combine_lpr = 64;  // combine lanes per output row
     bool combine_rows = false;  // one output row per combine workgroup, pieces over its waves
+    bool merge_in_kernel = false;  // the MFMA kernel merges split units itself (no combine launch)
     int ov = 0;
+    size_t ctr_bytes = 0;  // merge counters at the start of the workspace
+    size_t off_o = 0;
     size_t off_lse = 0;
     size_t ws_bytes = 0;
     bool empty = false;
@@ -176,6 +185,8 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "unknown kernel selector %d", desc->kernel);
     if (desc->num_workgroups < 0 || desc->num_cus < 0)
         return fail(DFLASH_ERR_INVALID_ARGUMENT, "num_workgroups / num_cus must be >= 0");
+    if (desc->merge_mode < DFLASH_MERGE_AUTO || desc->merge_mode > DFLASH_MERGE_IN_KERNEL)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "unknown merge_mode %d", desc->merge_mode);
 
     *p = Plan();
     if (desc->num_reqs == 0 || desc->total_q == 0) {
@@ -238,9 +249,18 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
         p->ov = tiles >= (int64_t)kChargeMinTiles * P ? kSegmentCharge : kSegmentChargeShort;
     }
     if (p->P > 1) {
-        const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(uint16_t);  // bf16 partials
-        p->off_lse = align_up(o_bytes);
+        // [merge counters, a fixed layout for every grid (merge.h)]
+        // [bf16 partials [P][2][rmax][Dp]] [fp32 log-sum-exps [P][2][rmax]]
+        const bool want = desc->merge_mode == DFLASH_MERGE_IN_KERNEL ||
+                          (desc->merge_mode == DFLASH_MERGE_AUTO && p->P <= kMergeInKernelAutoWgs);
+        p->merge_in_kernel = kernel == DFLASH_KERNEL_MFMA && want && p->P <= dflash::kMergeMaxWgs;
+        p->ctr_bytes = align_up((size_t)dflash::kCtrWords * sizeof(int32_t));
+        const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(uint16_t);
+        p->off_o = p->ctr_bytes;
+        p->off_lse = p->off_o + align_up(o_bytes);
         p->ws_bytes = p->off_lse + align_up((size_t)p->P * 2 * p->rmax * sizeof(float));
+        if (p->merge_in_kernel)
+            return DFLASH_OK;
         p->combine_lpr = kernel == DFLASH_KERNEL_MFMA ? dflash::combine_lanes_per_row(p->Dp, Hq) : 64;
         p->combine_wgs = dflash::combine_grid((int64_t)desc->total_q * Hq, p->combine_lpr);
         // Expected pieces per split unit: the runs over the units, plus the two that
@@ -344,8 +364,10 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.spans = span_offsets ? spans : nullptr;
     a.num_spans = span_offsets ? num_spans : 0;
     a.out = static_cast<uint16_t*>(out);
-    a.part_o = p.ws_bytes ? static_cast<uint16_t*>(desc->workspace) : nullptr;
-    a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(desc->workspace) + p.off_lse) : nullptr;
+    char* ws = static_cast<char*>(desc->workspace);
+    a.part_o = p.ws_bytes ? reinterpret_cast<uint16_t*>(ws + p.off_o) : nullptr;
+    a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
+    a.ctr = p.merge_in_kernel ? reinterpret_cast<uint32_t*>(ws) : nullptr;
     a.d.B = desc->num_reqs;
     a.d.Hkv = n_kv_heads;
     a.d.G = n_heads / n_kv_heads;
@@ -603,6 +625,7 @@ int dflash_block_attn_plan(const dflash_batch_desc* desc, int32_t n_heads, int32
     info->rows_per_unit = p.rmax;
     info->head_dim_padded = p.Dp;
     info->combine_workgroups = p.combine_wgs;
+    info->merge_in_kernel = p.merge_in_kernel ? 1 : 0;
     info->workspace_bytes = p.ws_bytes;
     return DFLASH_OK;
 }

@@ -38,7 +38,10 @@
 //    page-tail garbage (possibly NaN) is never loaded; their logits are masked,
 //    so their weight is exactly zero.
 //  * Epilogue: a unit finished inside the workgroup writes bf16 output;
-//    otherwise fp32 normalised partials + log2-sum-exp for combine.hip.
+//    otherwise its piece is a bf16 normalised partial + fp32 log2-sum-exp in the
+//    workgroup's workspace slot.  With merge counters (AttnArgs::ctr) the pieces'
+//    own workgroups merge each split unit after their runs (merge.h); without
+//    them combine.hip does.
 #pragma once
 
 #include <atomic>
@@ -46,6 +49,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "merge.h"
 
 namespace dflash {
 
@@ -162,7 +166,9 @@ struct Cfg {
     static constexpr int OFF_LSUM = OFF_K + K_BYTES;
     static constexpr int OFF_MREF = OFF_LSUM + ROWF_BYTES;
     static constexpr int OFF_FLAG = OFF_MREF + ROWF_BYTES;
-    static constexpr int LDS_BYTES = OFF_FLAG + 16 * 4;
+    // the split units of the run, for the in-kernel merge: [2 slots][16] int64
+    static constexpr int OFF_REC = OFF_FLAG + 16 * 4;
+    static constexpr int LDS_BYTES = OFF_REC + 2 * 16 * 8;
     // Epilogue staging of the unit's normalised rows as bf16, [row][d] with a 32-byte
     // pad per row, in the bytes the tile loop no longer uses (everything below LSUM).
     static constexpr int SROW = DP * 2 + 32;
@@ -170,7 +176,7 @@ struct Cfg {
     static_assert(ROWS * SROW <= OFF_LSUM, "epilogue staging must fit below the row sums");
     static_assert(KS >= 1 && DT >= 1, "head_dim too small for the d-split");
     static_assert(NCH >= 4 && NCH <= 16 && KPI * NCH == 64 && NI * KPI == kTK, "load geometry");
-    static_assert(RT <= 16, "flag array");
+    static_assert(RT <= 14, "flag array (the last two words carry the merge decision)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -236,6 +242,16 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first);
     if (begin >= end)
         return;
+    // The split units this run holds a piece of (slot 0: its first unit, slot 1: its
+    // last), kept in LDS for the in-kernel merge after the run (registers are full in
+    // the tile loop): per slot [0] the unit's first flat position, [1] its first
+    // workgroup (which names its counters), [2] its pieces, [3] the query tokens before
+    // its request, [4] its first row, [5] its rows, [6] its kv-head, [8] the arrival word
+    // before this piece's arrival; [7] of slot 0 is the run length per workgroup.
+    int64_t* rec_s = reinterpret_cast<int64_t*>(lds + C::OFF_REC);
+    int have_rec = 0;
+    if (a.ctr && threadIdx.x == 0)
+        rec_s[7] = tiles_per_wg(total, d.P);
 
     // Segments of this workgroup's run that a lazy pass abandoned (bit i: i-th segment;
     // segments past 63 share the overflow flag and are all recomputed).
@@ -685,18 +701,27 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     const int row = r0 + rsub;
                     if (row < rows_here) {
                         const u32x4_t x = *reinterpret_cast<const u32x4_t*>(stage + row * C::SROW + ch * 16);
-                        // streaming store: the combine reads the partial once, from HBM
-                        __builtin_nontemporal_store(x,
-                                                    reinterpret_cast<u32x4_t*>(a.part_o + (sbase + row) * DP + ch * 8));
+                        uint16_t* dst = a.part_o + (sbase + row) * DP + ch * 8;
+                        // merged in this kernel by other workgroups: coherent stores; merged by
+                        // the combine kernel: streaming stores (read once, from HBM)
+                        if (a.ctr)
+                            store16_coherent(dst, __builtin_bit_cast(uint4, x));
+                        else
+                            __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(dst));
                     }
                 }
                 if (wave == 0 && grp4 == 0) {
 #pragma unroll
                     for (int b = 0; b < RT; ++b) {
                         const float l = lsum_s[b * 16 + l16];
-                        a.part_lse[sbase + b * 16 + l16] = l > 0.f ? mref_s[b * 16 + l16] + log2f(l) : -INFINITY;
+                        const float lse = l > 0.f ? mref_s[b * 16 + l16] + log2f(l) : -INFINITY;
+                        if (a.ctr)
+                            store_f32_coherent(a.part_lse + sbase + b * 16 + l16, lse);
+                        else
+                            a.part_lse[sbase + b * 16 + l16] = lse;
                     }
                 }
+
             } else {
                 // The whole unit was here: bf16 output rows, real rows and columns only.
 #pragma unroll
@@ -713,12 +738,115 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 }
             }
             __syncthreads();
+            if (!whole && a.ctr) {
+                // record the piece; it is counted in after the run (below), when its stores
+                // have long completed -- a wait for them here would stall the run
+                if (threadIdx.x == 0) {
+                    const int64_t us = rbase + (int64_t)unit * g.uwork;
+                    const int64_t tpw = rec_s[7];
+                    int64_t kf, kl;
+                    unit_pieces(g, us, d.ov, tpw, kf, kl);
+                    int64_t* rp = rec_s + 16 * slot;
+                    rp[0] = us;
+                    rp[1] = kf;
+                    rp[2] = kl - kf + 1;
+                    rp[3] = qstart;
+                    rp[4] = row0;
+                    rp[5] = rows_here;
+                    rp[6] = kvh;
+                }
+                have_rec |= 1 << slot;
+            }
         }
     };
 
     walk(std::integral_constant<int, 0>{});
     if (redo_mask != 0 || redo_overflow)
         walk(std::integral_constant<int, 1>{});
+    if (!a.ctr)
+        return;  // the combine kernel merges the partials
+
+    // ---------------- in-kernel merge of the split units (merge.h) ----------------
+    // An item is the rows one wave merges at once (LPR lanes per row, 8 head-dim
+    // elements per lane).  Piece j of a unit merges items j, j + np, ...; its waves
+    // take every fourth of those.
+    constexpr int LPR = DP / 8;
+    constexpr int RPW = 64 / LPR;
+    const int rg = lane / LPR;
+    const int32_t d0 = (lane % LPR) * 8;
+    const bool dlive = EXACT || d0 < D;
+    // publish: every wave's partial rows and log-sum-exps have completed (vmcnt 0) before
+    // the barrier; then the pieces are counted in
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            if (have_rec & (1 << s))
+                rec_s[16 * s + 8] = __hip_atomic_fetch_add(a.ctr + kCtrArrive + rec_s[16 * s + 1], 1u,
+                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();  // the records in LDS
+    const int64_t tpw = rec_s[7];
+    auto merge_items = [&](const int64_t* rp, int64_t j) {
+        const int64_t us = rp[0], kf = rp[1], np = rp[2], qs = rp[3];
+        const int32_t row0 = (int32_t)rp[4], rows = (int32_t)rp[5], kvh = (int32_t)rp[6];
+        const int64_t nitems = (rows + RPW - 1) / RPW;
+        for (int64_t it = j + np * wave; it < nitems; it += np * WAVES) {
+            const int32_t rin = (int32_t)it * RPW + rg;
+            const bool live = rin < rows;
+            float acc[8];
+            const float W = merge_pieces<LPR, 16, true>(a.part_o, a.part_lse, d.rmax, DP, kf, np, np, us, tpw, rin,
+                                                        live, dlive, d0, acc);
+            if (live && dlive) {
+                const int32_t rr = row0 + rin;
+                const int32_t qi = rr / G;
+                const int32_t qj = rr % G;
+                store_merged(a.out + ((qs + qi) * a.Hq + (int64_t)kvh * G + qj) * D + d0, acc, W);
+            }
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if (!(have_rec & (1 << s)))
+            continue;
+        const int64_t* rp = rec_s + 16 * s;
+        const int64_t us = rp[0], kf = rp[1], np = rp[2];
+        const uint32_t old = (uint32_t)rp[8];
+        const int64_t me = logical_wg(blockIdx.x, d.P);
+        const bool last = (int64_t)(old & kArriveMask) == np - 1;
+        bool mine = true;
+        if (!last) {
+            // wave 0 waits for the unit (or gives up) for the whole workgroup
+            if (wave == 0) {
+                const bool go = wave_wait_or_give_up(a.ctr + kCtrArrive + kf, (uint32_t)np,
+                                                     a.ctr + kCtrGaveUp + 2 * me + s);
+                if (lane == 0)
+                    flag_s[14 + s] = go ? 1 : 0;
+            }
+            __syncthreads();
+            mine = flag_s[14 + s] != 0;
+        }
+        if (mine)
+            merge_items(rp, me - kf);
+        if (last && (old >> 16) != 0) {
+            // some pieces gave up before the unit completed: merge their items too
+            for (int64_t base = 0; base < np; base += 64) {
+                const int64_t k = kf + base + lane;
+                uint32_t g = 0;
+                if (base + lane < np)
+                    g = __hip_atomic_load(a.ctr + kCtrGaveUp + 2 * k + piece_slot(k, us, tpw), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                unsigned long long m = __ballot(g != 0);
+                while (m) {
+                    const int b = __ffsll((long long)m) - 1;
+                    m &= m - 1;
+                    merge_items(rp, base + b);
+                }
+            }
+        }
+        unit_depart(a.ctr, kf, np, [&](int64_t k) { return piece_slot(k, us, tpw); });
+    }
 }
 
 // Raises a kernel's dynamic-LDS limit once per device (not on every launch: a call

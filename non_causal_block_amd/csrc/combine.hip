@@ -15,6 +15,7 @@
 // waves taking every fourth piece, for units split many ways at head_dim 512.
 #include "device_common.h"
 #include "kernels.h"
+#include "merge.h"
 
 namespace dflash {
 
@@ -37,7 +38,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int lane = threadIdx.x & 63;
     const int rg = lane / LPR;  // row of this lane within the wave
     const int sl = lane % LPR;  // lane within the row's group
-    const int gbase = rg * LPR;
     const int64_t row0 = ((int64_t)blockIdx.x * kCombineWavesPerWg + wave) * RPW;
     if (row0 >= a.total_rows)
         return;
@@ -78,87 +78,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
             max_np = max(max_np, shfl_i64(max_np, lane ^ off));
     }
 
-    // Lane sl of a row's group holds piece kf + sl (+ LPR per round).  The
-    // log-sum-exps and the partial rows are requested together (rows of pieces that
-    // saw no key hold zeros, so they need no guard), and the weights are formed while
-    // the rows are in flight.
     const int32_t d0 = sl * 8;
     const bool dlive = split && d0 < a.D;
     float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        acc[e] = 0.f;
-    float M = -INFINITY;
-    float W = 0.f;
-    for (int64_t base = 0; base < max_np; base += LPR) {
-        const int64_t kq = kf + base + sl;
-        const float lse = (split && base + sl < npieces)
-                              ? a.part_lse[(kq * 2 + piece_slot(kq, us, tpw)) * d.rmax + rin]
-                              : -INFINITY;
-        const int cnt = (int)max<int64_t>(0, min<int64_t>(LPR, npieces - base));
-        int max_cnt = cnt;
-        if constexpr (RPW > 1) {
-#pragma unroll
-            for (int off = 32; off >= LPR; off >>= 1)
-                max_cnt = max(max_cnt, __shfl_xor(max_cnt, off));
-        }
-        float wl = 0.f;
-        for (int j0 = 0; j0 < max_cnt; j0 += PPS) {
-            uint4 x[PPS];
-#pragma unroll
-            for (int u = 0; u < PPS; ++u) {
-                const int64_t k = kf + base + j0 + u;
-                const int64_t prow = (k * 2 + piece_slot(k, us, tpw)) * d.rmax + rin;
-                x[u] = (dlive && j0 + u < cnt) ? *reinterpret_cast<const uint4*>(a.part_o + prow * a.Dp + d0)
-                                               : make_uint4(0, 0, 0, 0);
-            }
-            if (j0 == 0) {
-                // weights of this round, formed while the rows above are in flight; what
-                // earlier rounds summed (more than LPR pieces only) is rescaled to the new max
-                float mr = lse;
-#pragma unroll
-                for (int off = LPR / 2; off >= 1; off >>= 1)
-                    mr = fmaxf(mr, __shfl_xor(mr, off));
-                const float m_new = fmaxf(M, mr);
-                if (base > 0 && m_new > M) {
-                    const float sc = exp2f(M - m_new);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        acc[e] *= sc;
-                    W *= sc;
-                }
-                M = m_new;
-                wl = (lse == -INFINITY) ? 0.f : exp2f(lse - M);
-                W += wl;
-            }
-#pragma unroll
-            for (int u = 0; u < PPS; ++u) {
-                const int src = gbase + min(j0 + u, LPR - 1);
-                const float wsh = __shfl(wl, src);
-                const float wj = (j0 + u < cnt) ? wsh : 0.f;
-                const uint32_t w4[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // bf16 -> fp32 is exact: the bits move to the high half
-                    acc[2 * e] = fmaf(wj, __uint_as_float(w4[e] << 16), acc[2 * e]);
-                    acc[2 * e + 1] = fmaf(wj, __uint_as_float(w4[e] & 0xffff0000u), acc[2 * e + 1]);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1)
-        W += __shfl_xor(W, off);
-    if (dlive) {
-        const float inv = W > 0.f ? 1.f / W : 0.f;
-        uint16_t* dst = a.out + (t * a.Hq + h) * (int64_t)a.D + d0;
-        uint4 packed;
-        packed.x = (uint32_t)f32_to_bf16(acc[0] * inv) | ((uint32_t)f32_to_bf16(acc[1] * inv) << 16);
-        packed.y = (uint32_t)f32_to_bf16(acc[2] * inv) | ((uint32_t)f32_to_bf16(acc[3] * inv) << 16);
-        packed.z = (uint32_t)f32_to_bf16(acc[4] * inv) | ((uint32_t)f32_to_bf16(acc[5] * inv) << 16);
-        packed.w = (uint32_t)f32_to_bf16(acc[6] * inv) | ((uint32_t)f32_to_bf16(acc[7] * inv) << 16);
-        *reinterpret_cast<uint4*>(dst) = packed;
-    }
+    const float W = merge_pieces<LPR, PPS>(a.part_o, a.part_lse, d.rmax, a.Dp, kf, npieces, max_np, us, tpw, rin,
+                                           split, dlive, d0, acc);
+    if (dlive)
+        store_merged(a.out + (t * a.Hq + h) * (int64_t)a.D + d0, acc, W);
 }
 
 // One output row per workgroup, its pieces dealt over the four waves (wave w takes

@@ -154,10 +154,11 @@ DFL_HD void query_range(int32_t L, int32_t n, int32_t i, bool causal, int32_t wi
 }
 
 // High end of a causal row's range once bidirectional spans are applied: a
-// query at position p inside a span [s, e) also sees the span's later keys
-// (the mm-prefix case -- a multimodal prefix is attended as a whole while
-// text stays causal; kenforever1 "DFlash + Gemma 4 31B-it" notes, section on
-// MooreThreads/vllm-musa PR #52).  The request's spans are entries
+// query at position p inside a span [s, e) also sees the span's later keys.
+// This rule is a reading: kenforever1 "DFlash + Gemma 4 31B-it" notes, section
+// on MooreThreads/vllm-musa PR #52, only name the backend's mm-prefix support;
+// the rule is the plainest mask in which a multimodal prefix is attended as a
+// whole while text stays causal.  The request's spans are entries
 // offs[r] .. offs[r+1]-1 of `spans` ((start, end) pairs); entries outside
 // [0, num_spans) are ignored, and the result never passes T - 1.  Any order
 // and any overlap give the same answer: the largest end among the spans that

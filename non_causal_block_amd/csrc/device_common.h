@@ -261,6 +261,10 @@ struct AttnArgs {
     uint16_t* out;
     uint16_t* part_o;  // bf16 [P][2][rmax][Dp]: normalised partial outputs
     float* part_lse;   // [P][2][rmax]
+    // Counters of the in-kernel merge of split units (layout in merge.h); zero before
+    // the launch and zero again after it.  nullptr: the kernel leaves the partials for
+    // the combine kernel.
+    uint32_t* ctr;
     Decomp d;
     int32_t Hq;
     int32_t D;         // real head_dim

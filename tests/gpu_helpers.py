@@ -36,7 +36,7 @@ def upload(wl: workloads.Workload) -> dict:
 
 
 def run(wl: workloads.Workload, t: dict = None, *, kernel=nb.DFLASH_KERNEL_AUTO, num_workgroups=0,
-        hints=True, causal_none=False, out=None, spans=None) -> torch.Tensor:
+        hints=True, causal_none=False, out=None, spans=None, merge_mode=nb.DFLASH_MERGE_AUTO) -> torch.Tensor:
     """``spans``: per-request (start, end) lists -> dflash_block_attn_spans."""
     t = t or upload(wl)
     so = sp = None
@@ -50,7 +50,7 @@ def run(wl: workloads.Workload, t: dict = None, *, kernel=nb.DFLASH_KERNEL_AUTO,
                       causal=None if causal_none else t["causal"], window=wl.window, scale=wl.scale, out=out,
                       max_block_len=int(wl.block_lens.max()) if (hints and wl.B) else 0,
                       total_kv_len=wl.total_kv if hints else 0, kernel=kernel, num_workgroups=num_workgroups,
-                      span_offsets=so, spans=sp)
+                      span_offsets=so, spans=sp, merge_mode=merge_mode)
     torch.cuda.synchronize()
     return o
 

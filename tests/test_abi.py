@@ -56,7 +56,7 @@ def test_debug_check_switch_and_argument_errors(lib):
 
 
 def test_abi_version(lib):
-    assert nb.dflash_abi_version() == 1
+    assert nb.dflash_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -204,10 +204,17 @@ def test_plan_mfma_global_layer(lib):
     assert p.kernel == nb.DFLASH_KERNEL_MFMA
     assert p.rows_per_unit == 80 and p.head_dim_padded == 512 and p.tile_keys == 32
     assert p.num_workgroups == 256  # planning without a device assumes one workgroup per CU
-    # two slots per workgroup: bf16 partial rows and fp32 log-sum-exps
-    assert p.workspace_bytes >= p.num_workgroups * 2 * 80 * 512 * 2 + p.num_workgroups * 2 * 80 * 4
-    # 16 units over 256 runs: about 18 pieces each, so one combine workgroup per output row
-    assert p.combine_workgroups == 36 * 32
+    # merge counters (arrivals, claims per workgroup, one finish count), then two slots per
+    # workgroup: bf16 partial rows and fp32 log-sum-exps
+    P = p.num_workgroups
+    assert p.workspace_bytes >= (2 * P + 1) * 4 + P * 2 * 80 * 512 * 2 + P * 2 * 80 * 4
+    # a grid of 256: the combine kernel merges (16 units over 256 runs, about 18 pieces each,
+    # so one combine workgroup per output row)
+    assert p.merge_in_kernel == 0 and p.combine_workgroups == 36 * 32
+    # asked for the in-kernel merge: no combine launch, same workspace
+    p2 = nb.dflash_block_attn_plan(desc(merge_mode=nb.DFLASH_MERGE_IN_KERNEL), 32, 4, 512)
+    assert p2.merge_in_kernel == 1 and p2.combine_workgroups == 0
+    assert p2.workspace_bytes == p.workspace_bytes
 
 
 def test_plan_small_problem_uses_few_workgroups(lib):
@@ -216,12 +223,19 @@ def test_plan_small_problem_uses_few_workgroups(lib):
     # 17 tiles per kv-head, two kv-heads: two tiles per workgroup, not the whole chip
     assert p.num_workgroups == 17
     assert p.head_dim_padded == 128 and p.rows_per_unit == 48
+    # a small grid merges its split units inside the attention kernel (one launch)
+    assert p.merge_in_kernel == 1 and p.combine_workgroups == 0
+    p2 = nb.dflash_block_attn_plan(desc(num_reqs=1, total_q=9, total_kv_len=521, max_pages_per_req=33, num_pages=34,
+                                        merge_mode=nb.DFLASH_MERGE_COMBINE_KERNEL), 8, 2, 128)
+    assert p2.merge_in_kernel == 0 and p2.combine_workgroups > 0
 
 
 def test_plan_reference_kernel_and_forced_grid(lib):
     p = nb.dflash_block_attn_plan(desc(kernel=nb.DFLASH_KERNEL_REFERENCE, num_workgroups=37), 32, 4, 200)
     assert p.kernel == nb.DFLASH_KERNEL_REFERENCE and p.num_workgroups == 37
     assert p.rows_per_unit == 16 and p.head_dim_padded == 200
+    # the reference kernel always leaves its partials to the combine kernel
+    assert p.merge_in_kernel == 0 and p.combine_workgroups > 0
     p1 = nb.dflash_block_attn_plan(desc(num_workgroups=1), 32, 4, 512)
     assert p1.workspace_bytes == 0 and p1.combine_workgroups == 0
 
@@ -262,3 +276,9 @@ def test_page_elements_limit(lib):
     # just below the limit the same shape is accepted by the planner
     p = nb.dflash_block_attn_plan(desc(page_size=1024, max_pages_per_req=100), 4095, 4095, 512)
     assert p.num_workgroups >= 1
+
+
+def test_merge_mode_is_checked(lib):
+    d = desc()
+    d.merge_mode = 3
+    expect(call(d), nb.DFLASH_ERR_INVALID_ARGUMENT, "merge_mode")

@@ -45,7 +45,7 @@ def _desc(wl, workspace=None):
                      total_kv_len=wl.total_kv, page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req,
                      num_pages=wl.num_pages)
     need = nb.dflash_block_attn_workspace_size(d, wl.Hq, wl.Hkv, wl.D)
-    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=dev())
+    ws = workspace if workspace is not None else torch.zeros(max(need, 256), dtype=torch.uint8, device=dev())
     d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
     return d, ws
 

@@ -35,7 +35,7 @@ def _call(wl, t, *, num_pages=None, total_q=None, out=None, span_offsets=None, s
                         page_size=wl.page_size, max_pages_per_req=wl.page_table.shape[1],
                         num_pages=wl.num_pages if num_pages is None else num_pages)
     need = nb.dflash_block_attn_workspace_size(desc, wl.Hq, wl.Hkv, wl.D)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=d)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=d)
     desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
     out = torch.full((wl.total_q, wl.Hq, wl.D), 7.0, dtype=torch.bfloat16, device=d) if out is None else out
     stream = torch.cuda.current_stream().cuda_stream

@@ -232,8 +232,9 @@ def test_more_than_64_requests(kname, kernel):
         H.assert_parity(got, ref, f"B=130 kernel={kname} wg={nwg}")
 
 
+@pytest.mark.parametrize("merge", ["combine", "in-kernel"])
 @pytest.mark.parametrize("D,L0", [(128, 8000), (512, 12000)])
-def test_combine_over_more_than_64_pieces(D, L0):
+def test_combine_over_more_than_64_pieces(D, L0, merge):
     """A unit split over hundreds of workgroups: the combine merges its pieces in
     rounds of 64 (rescaling earlier rounds to the running maximum).  One long request
     and one kv-head, so 600 workgroups take about one tile each.  At head_dim 128 one
@@ -241,9 +242,10 @@ def test_combine_over_more_than_64_pieces(D, L0):
     fourth piece per wave (375 pieces: more than 64 per wave)."""
     wl = workloads.build(2, 8, 1, D, [L0, 300], [9, 5], [0, 1], seed=31)
     ref = oracle.run_workload(wl)
+    mode = nb.DFLASH_MERGE_COMBINE_KERNEL if merge == "combine" else nb.DFLASH_MERGE_IN_KERNEL
     for nwg in (150, 600):
-        got = H.to_f64(H.run(wl, num_workgroups=nwg))
-        H.assert_parity(got, ref, f"many pieces D={D} wg={nwg}")
+        got = H.to_f64(H.run(wl, num_workgroups=nwg, merge_mode=mode))
+        H.assert_parity(got, ref, f"many pieces D={D} wg={nwg} merge={merge}")
 
 
 def test_page_permutation_invariance_is_bitwise():
@@ -293,7 +295,7 @@ def test_timing_events_are_recorded():
     d = nb.make_desc(num_reqs=wl.B, total_q=wl.total_q, max_block_len=9, total_kv_len=wl.total_kv,
                      page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req, num_pages=wl.num_pages)
     need = nb.dflash_block_attn_workspace_size(d, wl.Hq, wl.Hkv, wl.D)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=H.dev())
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=H.dev())
     d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
     d.event_attn_begin, d.event_attn_end = ev0.cuda_event, ev1.cuda_event
     out = torch.empty((wl.total_q, wl.Hq, wl.D), dtype=torch.bfloat16, device=H.dev())
