@@ -203,6 +203,26 @@ int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new
                              int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, const uint8_t* causal,
                              int32_t window, float scale, void* out, void* stream, const dflash_batch_desc* desc);
 
+/*
+ * dflash_block_attn for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same operation,
+ * arguments, layouts and errors, but the scratch comes from a static array inside the
+ * library -- desc->workspace and desc->workspace_bytes are ignored, and the split-KV pieces
+ * are always merged by the combine kernel (desc->merge_mode is ignored).  The array holds
+ * dflash_noalloc_scratch_bytes() bytes (48 MiB) on every GPU the library runs on, for the
+ * life of the process; a call that needs more (dflash_block_attn_workspace_size) returns
+ * DFLASH_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  Every call on one GPU shares
+ * the array: calls that may overlap on one GPU (different streams, or host threads) race
+ * and must not be issued.  Nothing is allocated, freed or synchronised.
+ */
+int dflash_block_attn_noalloc(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                              const int32_t* ctx_lens, const int32_t* block_lens, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim, const uint8_t* causal, int32_t window,
+                              float scale, void* out, void* stream, const dflash_batch_desc* desc);
+
+/* Bytes of the static scratch dflash_block_attn_noalloc uses on each GPU. */
+size_t dflash_noalloc_scratch_bytes(void);
+
 /* Scratch bytes dflash_block_attn needs for this desc and shape (desc->workspace is ignored). */
 int dflash_block_attn_workspace_size(const dflash_batch_desc* desc, int32_t n_heads, int32_t n_kv_heads,
                                      int32_t head_dim, size_t* bytes);

@@ -134,6 +134,19 @@ def dflash_block_attn(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_h
                                          scale, _ptr(out), stream, ctypes.byref(desc))
 
 
+def dflash_block_attn_noalloc(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads: int, n_kv_heads: int,
+                              head_dim: int, causal, window: int, scale: float, out, stream: Optional[int],
+                              desc: dflash_batch_desc) -> int:
+    """Raw call on the library's static scratch (no workspace, nothing allocated); status code out."""
+    return _lib.load().dflash_block_attn_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table),
+                                                 _ptr(ctx_lens), _ptr(block_lens), n_heads, n_kv_heads, head_dim,
+                                                 _ptr(causal), window, scale, _ptr(out), stream, ctypes.byref(desc))
+
+
+def dflash_noalloc_scratch_bytes() -> int:
+    return int(_lib.load().dflash_noalloc_scratch_bytes())
+
+
 def dflash_block_attn_spans(q, k_pages, v_pages, page_table, ctx_lens, block_lens, n_heads: int, n_kv_heads: int,
                             head_dim: int, causal, span_offsets, spans, num_spans: int, window: int, scale: float,
                             out, stream: Optional[int], desc: dflash_batch_desc) -> int:

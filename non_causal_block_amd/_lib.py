@@ -77,6 +77,11 @@ def load() -> ctypes.CDLL:
     lib.dflash_block_attn.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, i32, ctypes.c_float, P, P,
                                       ctypes.POINTER(dflash_batch_desc)]
     lib.dflash_block_attn.restype = ctypes.c_int
+    lib.dflash_block_attn_noalloc.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, i32, ctypes.c_float, P, P,
+                                              ctypes.POINTER(dflash_batch_desc)]
+    lib.dflash_block_attn_noalloc.restype = ctypes.c_int
+    lib.dflash_noalloc_scratch_bytes.argtypes = []
+    lib.dflash_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.dflash_block_attn_spans.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P, P, i32, i32, ctypes.c_float, P,
                                             P, ctypes.POINTER(dflash_batch_desc)]
     lib.dflash_block_attn_spans.restype = ctypes.c_int

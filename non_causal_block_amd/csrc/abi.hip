@@ -482,6 +482,16 @@ int append_prepare(const void* k_new, const void* v_new, void* k_pages, void* v_
 
 }  // namespace
 
+namespace dflash {
+
+// The thread's last-error text, for entry points in other translation units.
+int set_last_error(int status, const char* msg)
+{
+    return fail(status, "%s", msg);
+}
+
+}  // namespace dflash
+
 extern "C" {
 
 int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }

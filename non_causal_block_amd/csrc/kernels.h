@@ -40,6 +40,9 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // DFlash2 in-block grouped dynamic depthwise convolution
 hipError_t launch_block_conv(const ConvArgs& a, hipStream_t stream);
 
+// records `msg` as the calling thread's last error (dflash_last_error_message); returns status
+int set_last_error(int status, const char* msg);
+
 // debug checks: the per-device state word (static device memory) and the checking kernel
 hipError_t debug_state_ptr(uint32_t** out);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);

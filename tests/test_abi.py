@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
 
