@@ -35,6 +35,9 @@ at draft-step shapes and prints its own JSON line.
     python bench.py --summarize-pmc FETCH_CSV WRITE_CSV
 turns two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE)
 into the HBM-traffic record the "traffic" field reads.
+
+    python bench.py --summarize-trace KERNEL_TRACE_CSV
+prints kernel durations from a rocprofv3 kernel trace, per kernel and per phase.
 """
 from __future__ import annotations
 
@@ -83,7 +86,10 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
 
     import oracle
 
-    oracle.build()
+    # the oracle library is compiled before the GPU is touched (main); a compiler must not
+    # be started from this process now
+    if not oracle.is_built():
+        raise RuntimeError("the oracle library is missing or stale; build it before initialising the GPU")
     threads = oracle.default_threads()
     rng = np.random.default_rng(0)
     all_rows = wl.total_q * wl.Hq
@@ -127,6 +133,36 @@ def _pmc_means(path: str, counter: str) -> dict:
                 continue
             acc.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_trace(csv_path: str) -> dict:
+    """Kernel durations from a rocprofv3 --kernel-trace CSV, per kernel name and per
+    phase (phases are separated by idle gaps of more than 5 ms, e.g. the eager calls
+    and the graph replays of --graph-latency)."""
+    import csv
+
+    import numpy as np
+
+    rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                  for r in csv.DictReader(open(csv_path)))
+    phases, cur, last_end = [], [], None
+    for s, e, n in rows:
+        if last_end is not None and s - last_end > 5_000_000:
+            phases.append(cur)
+            cur = []
+        cur.append((s, e, n))
+        last_end = e if last_end is None else max(last_end, e)
+    phases.append(cur)
+    out = []
+    for i, ph in enumerate(phases):
+        per = {}
+        for s, e, n in ph:
+            per.setdefault(n.split("(")[0][:120], []).append((e - s) / 1e3)
+        out.append({"phase": i, "kernels": {n: {"count": len(v), "mean_us": float(np.mean(v)),
+                                                "median_us": float(np.median(v)),
+                                                "p10_us": float(np.percentile(v, 10)),
+                                                "p90_us": float(np.percentile(v, 90))} for n, v in per.items()}})
+    return {"trace": csv_path, "phases": out}
 
 
 def gpu_info() -> dict:
@@ -177,11 +213,41 @@ def summarize_pmc(fetch_csv: str, write_csv: str, config: str) -> dict:
     }
 
 
-def graph_latency(reps: int = 200) -> dict:
+def _graph_node_types(graph) -> list:
+    """Node types of a captured HIP graph (torch CUDAGraph kept with keep_graph=True),
+    read with the HIP runtime torch loaded."""
+    import ctypes
+
+    import torch
+
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    P = ctypes.c_void_p
+    hip.hipGraphGetNodes.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(ctypes.c_size_t)]
+    hip.hipGraphNodeGetType.argtypes = [P, ctypes.POINTER(ctypes.c_int)]
+    names = {0: "kernel", 1: "memcpy", 2: "memset", 3: "host", 4: "graph", 5: "empty", 6: "wait_event",
+             7: "event_record", 10: "mem_alloc", 11: "mem_free"}
+    g = P(graph.raw_cuda_graph())
+    n = ctypes.c_size_t(0)
+    if hip.hipGraphGetNodes(g, None, ctypes.byref(n)) != 0:
+        return ["?"]
+    arr = (P * n.value)()
+    hip.hipGraphGetNodes(g, arr, ctypes.byref(n))
+    out = []
+    for i in range(n.value):
+        t = ctypes.c_int(-1)
+        hip.hipGraphNodeGetType(arr[i], ctypes.byref(t))
+        out.append(names.get(t.value, str(t.value)))
+    return out
+
+
+def graph_latency(reps: int = 200, only: str = "") -> dict:
     """Per-call latency of dflash_block_attn_append, eager vs graph replay.
 
     Each call is timed alone from the host (launch to completion, warm caches:
-    a draft step re-reads the context it just read) and on the GPU (events)."""
+    a draft step re-reads the context it just read) and on the GPU (events).  The
+    captured graph's node types are listed, and a control -- one trivial torch
+    kernel, eager vs replayed graph -- measures what a graph replay costs on this
+    runtime by itself.  ``only`` ("c1:1", ...) restricts the shapes."""
     import numpy as np
     import torch
 
@@ -197,9 +263,28 @@ def graph_latency(reps: int = 200) -> dict:
     def t16(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    side = torch.cuda.Stream()
+
+    def timed(fn):
+        host, gpu = [], []
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(reps + 10):
+            t0 = time.perf_counter()
+            e0.record(side)
+            fn()
+            e1.record(side)
+            side.synchronize()
+            t1 = time.perf_counter()
+            if i >= 10:
+                host.append((t1 - t0) * 1e6)
+                gpu.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(host)), float(np.median(gpu))
+
     results = []
     for name, sh in shapes.items():
         for B in (1, 2, 4, 8):
+            if only and f"{name}:{B}" != only:
+                continue
             rng = np.random.default_rng(2000 + B)
             ctx = sh["ctx"](rng, B)
             wl = workloads.build(B, sh["Hq"], sh["Hkv"], sh["D"], ctx, np.full(B, 9), np.zeros(B, dtype=np.uint8),
@@ -215,7 +300,6 @@ def graph_latency(reps: int = 200) -> dict:
                              dtype=torch.uint8, device=dev)
             desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
             plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
-            side = torch.cuda.Stream()
 
             def call():
                 st = nb.dflash_block_attn_append(q, kn, vn, kp, vp, pt, cl, bl, wl.Hq, wl.Hkv, wl.D, None, 0,
@@ -227,38 +311,45 @@ def graph_latency(reps: int = 200) -> dict:
                 for _ in range(10):
                     call()
             torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
+            g = torch.cuda.CUDAGraph(keep_graph=True)
             with torch.cuda.graph(g, stream=side):
                 call()
+            g.instantiate()
             torch.cuda.synchronize()
-
-            def timed(fn):
-                host, gpu = [], []
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                for i in range(reps + 10):
-                    t0 = time.perf_counter()
-                    e0.record(side)
-                    fn()
-                    e1.record(side)
-                    side.synchronize()
-                    t1 = time.perf_counter()
-                    if i >= 10:
-                        host.append((t1 - t0) * 1e6)
-                        gpu.append(e0.elapsed_time(e1) * 1e3)
-                return float(np.median(host)), float(np.median(gpu))
-
+            nodes = _graph_node_types(g)
             with torch.cuda.stream(side):
                 eager_host, eager_gpu = timed(call)
+                torch.cuda.synchronize()
+                time.sleep(0.01)  # separates the eager calls from the replays in a kernel trace
                 graph_host, graph_gpu = timed(g.replay)
             results.append({"shape": name, "B": B, "query_tokens": wl.total_q, "Hq": wl.Hq, "Hkv": wl.Hkv,
                             "head_dim": wl.D, "total_kv_tokens": wl.total_kv, "attn_workgroups": plan.num_workgroups,
-                            "combine": plan.combine_workgroups > 0,
+                            "merge_in_kernel": bool(plan.merge_in_kernel), "graph_nodes": nodes,
                             "eager_us": eager_host, "graph_us": graph_host,
                             "eager_gpu_us": eager_gpu, "graph_gpu_us": graph_gpu})
             print(f"[graph] {name} B={B}: eager {eager_host:.1f} us (gpu {eager_gpu:.1f}), "
-                  f"graph {graph_host:.1f} us (gpu {graph_gpu:.1f})", file=sys.stderr, flush=True)
+                  f"graph {graph_host:.1f} us (gpu {graph_gpu:.1f}), nodes {nodes}", file=sys.stderr, flush=True)
+    # control: one trivial torch kernel, eager vs replayed graph
+    x = torch.zeros(16, device=dev)
+    with torch.cuda.stream(side):
+        for _ in range(10):
+            x.add_(1)
+    torch.cuda.synchronize()
+    gc = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gc, stream=side):
+        x.add_(1)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        ctl_eager = timed(lambda: x.add_(1))
+        ctl_graph = timed(gc.replay)
+    control = {"what": "one trivial torch kernel (x.add_(1)), eager vs replayed graph",
+               "eager_us": ctl_eager[0], "graph_us": ctl_graph[0], "eager_gpu_us": ctl_eager[1],
+               "graph_gpu_us": ctl_graph[1]}
+    print(f"[graph] control: eager gpu {ctl_eager[1]:.1f} us, graph gpu {ctl_graph[1]:.1f} us", file=sys.stderr,
+          flush=True)
     return {"metric": "draft-step latency: block K/V append + attention, one call, us (median)",
-            "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": results}
+            "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": results,
+            "control": control}
 
 
 def conv_bench(reps: int = 200) -> dict:
@@ -319,9 +410,16 @@ def main(argv=None) -> int:
                     help="how split-KV pieces are merged (desc->merge_mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV")
     ap.add_argument("--graph-latency", action="store_true")
+    ap.add_argument("--graph-shape", default="", help="with --graph-latency: only this shape, e.g. c1:1")
+    ap.add_argument("--graph-reps", type=int, default=200)
     ap.add_argument("--conv", action="store_true")
     args = ap.parse_args(argv)
+
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
+        return 0
 
     if args.summarize_pmc:
         rec = summarize_pmc(*args.summarize_pmc, args.config)
@@ -353,7 +451,8 @@ def main(argv=None) -> int:
 
     if args.graph_latency or args.conv:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
-        print(json.dumps(graph_latency() if args.graph_latency else conv_bench()), flush=True)
+        print(json.dumps(graph_latency(args.graph_reps, args.graph_shape) if args.graph_latency else conv_bench()),
+              flush=True)
         return 0
 
     if not os.path.exists(nb._lib.LIB_PATH):

@@ -196,7 +196,10 @@ int dflash_block_kv_append(const void* k_new, const void* v_new, void* k_pages, 
  * dflash_block_kv_append followed by dflash_block_attn on the same stream: one
  * call per draft step, graph-capturable (it allocates nothing, synchronises
  * nothing and enqueues only kernel launches).  Both halves are validated before
- * either is enqueued; arguments as for the two calls.
+ * either is enqueued; arguments as for the two calls.  With the MFMA kernel and
+ * pages of at least 16 keys the two are one launch: the attention reads the
+ * block's own K/V from k_new / v_new and writes them into the pages itself (the
+ * result, pages included, is the same as the two calls').
  */
 int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                              const int32_t* page_table, const int32_t* ctx_lens, const int32_t* block_lens,

@@ -368,6 +368,9 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.part_o = p.ws_bytes ? reinterpret_cast<uint16_t*>(ws + p.off_o) : nullptr;
     a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
     a.ctr = p.merge_in_kernel ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+    a.k_new = a.v_new = nullptr;  // set by dflash_block_attn_append for the fused launch
+    a.k_dst = a.v_dst = nullptr;
+    a.app_dk = a.app_dv = 0;
     a.d.B = desc->num_reqs;
     a.d.Hkv = n_kv_heads;
     a.d.G = n_heads / n_kv_heads;
@@ -393,7 +396,8 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     return DFLASH_OK;
 }
 
-int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t s, bool validate = true)
+int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t s, bool validate = true,
+                bool fused_append = false)
 {
     const Plan& p = call.plan;
     const dflash::AttnArgs& a = call.args;
@@ -404,8 +408,9 @@ int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t
     }
     if (desc->event_attn_begin && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_begin), s) != hipSuccess)
         return fail(DFLASH_ERR_HIP, "hipEventRecord(event_attn_begin) failed");
-    hipError_t e = p.kernel == DFLASH_KERNEL_MFMA ? dflash::launch_attn_mfma(a, p.Dp, p.row_tiles, s)
-                                                  : dflash::launch_attn_ref(a, s);
+    hipError_t e = fused_append ? dflash::launch_attn_mfma_append(a, p.Dp, p.row_tiles, s)
+                   : p.kernel == DFLASH_KERNEL_MFMA ? dflash::launch_attn_mfma(a, p.Dp, p.row_tiles, s)
+                                                    : dflash::launch_attn_ref(a, s);
     if (e != hipSuccess)
         return fail(DFLASH_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
     if (desc->event_attn_end && hipEventRecord(static_cast<hipEvent_t>(desc->event_attn_end), s) != hipSuccess)
@@ -714,6 +719,20 @@ int dflash_block_attn_append(const void* q, const void* k_new, const void* v_new
         const hipError_t ev = dflash::launch_validate(v, s);
         if (ev != hipSuccess)
             return fail(DFLASH_ERR_HIP, "debug-check kernel launch failed: %s", hipGetErrorString(ev));
+    }
+    // The MFMA kernel with pages of >= 16 keys takes the append into its own launch: it
+    // reads the block's K/V rows from k_new / v_new and writes them into the pages.
+    const bool fused = !c.plan.empty && c.plan.kernel == DFLASH_KERNEL_MFMA && c.args.page_shift >= 4;
+    if (fused) {
+        c.args.k_new = ap.k_new;
+        c.args.v_new = ap.v_new;
+        c.args.k_dst = ap.k_pages;
+        c.args.v_dst = ap.v_pages;
+        const intptr_t dk = reinterpret_cast<intptr_t>(ap.k_new) - reinterpret_cast<intptr_t>(ap.k_pages);
+        const intptr_t dv = reinterpret_cast<intptr_t>(ap.v_new) - reinterpret_cast<intptr_t>(ap.v_pages);
+        c.args.app_dk = (int64_t)(dk / 2);  // all four are 16-byte aligned
+        c.args.app_dv = (int64_t)((dv - dk) / 2);
+        return attn_launch(c, desc, s, /*validate=*/false, /*fused_append=*/true);
     }
     if (ap.total_rows > 0) {
         const hipError_t e = dflash::launch_kv_append(ap, s);

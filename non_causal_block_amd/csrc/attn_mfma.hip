@@ -27,7 +27,7 @@ static int occupancy_one()
     if (blocks >= 0)
         return blocks;
     if (ensure_lds_limit<DP, RT, EXACT, false, true>() != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT, false, true>,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_mfma_kernel<DP, RT, EXACT, false, true, false>,
                                                      Cfg<DP, RT>::THREADS, Cfg<DP, RT>::LDS_BYTES) != hipSuccess)
         return 0;
     cached.store(blocks, std::memory_order_release);

@@ -182,11 +182,14 @@ struct Cfg {
 
 // EXACT: head_dim == DP, so every d-chunk exists and no lane needs masking.
 // SPANS: causal rows may be widened by bidirectional spans (a.span_offsets).
+// APPEND: the block's own K/V (keys L..T-1) are read from a.k_new / a.v_new instead of
+// the pages, and the workgroup that finishes a (request, kv-head)'s last tile writes them
+// into the pages (the block K/V append of a draft step, fused into the same launch).
 // WIDEPG: pages hold at least 16 keys, so a 32-key tile lies in at most two pages
 // whose ids are wave-uniform.  (Smaller pages are a separate instance: a runtime
 // branch between the two ways of locating keys made the compiler wait for the
 // tile's LDS stores before every key address on the common path.)
-template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG>
+template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG, bool APPEND>
 __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 {
     using C = Cfg<DP, RT>;
@@ -327,8 +330,15 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
             const int32_t hkvd = d.Hkv * D;  // elements per key row
             // element offset of this lane's 16 bytes inside a key row (< hkvd)
             const int32_t lane_off = (int32_t)head_off + (lval ? wbase + 8 * sl : 0);
+            // APPEND: keys from app_from on are the block's own, read from k_new / v_new:
+            // element offsets relative to k_pages (v_pages for V, which adds app_dv)
+            const int32_t app_from = APPEND ? L : INT32_MAX;
+            const int64_t app_base = APPEND ? a.app_dk + (qstart - L) * (int64_t)hkvd + lane_off : 0;
+            uint32_t blkmask = 0;  // APPEND: bit i -- this lane's i-th key of the tile is a block key
             auto tile_rows = [&](int32_t t, int32_t pgl, int64_t (&rows)[NI]) {
                 const int32_t k0 = g.kv_lo + t * kTK;
+                if constexpr (APPEND)
+                    blkmask = 0;
                 if constexpr (WIDEPG) {
                     // Keys 0-15 of the tile lie in the page of its key 0, keys 16-31 in that
                     // of its key 16 (tiles start at multiples of 32; a clamped key T - 1
@@ -346,6 +356,11 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                         const int32_t key = min(k0 + i * KPI + kl, T - 1);
                         const uint32_t inpg = (uint32_t)(key & (psize - 1)) * (uint32_t)hkvd + (uint32_t)lane_off;
                         rows[i] = (((i * KPI) & 16) ? base1 : base0) + inpg;
+                        if constexpr (APPEND) {
+                            const bool blk = key >= app_from;
+                            rows[i] = blk ? app_base + (int64_t)key * hkvd : rows[i];
+                            blkmask |= (blk ? 1u : 0u) << i;
+                        }
                     }
                 } else {
 #pragma unroll
@@ -440,6 +455,16 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     for (int i = 0; i < NI; ++i)
                         dst[i] = ldg16_stream(base + rows[i]);
                 };
+                // V: as K, except that block keys (APPEND) are read from v_new
+                auto issue_v = [&](u32x4_t (&dst)[NI]) {
+                    if constexpr (APPEND) {
+#pragma unroll
+                        for (int i = 0; i < NI; ++i)
+                            dst[i] = ldg16_stream(a.v_pages + rows[i] + (((blkmask >> i) & 1u) ? a.app_dv : 0));
+                    } else {
+                        issue(a.v_pages, dst);
+                    }
+                };
 
                 // One 32-key tile per step.  At the top of step t the registers holding the
                 // K/V of tile t are written to LDS and at once refilled with tile t+1, which
@@ -455,7 +480,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 issue(a.k_pages, kr);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (MODE != kMaxScan)
-                    issue(a.v_pages, vr);
+                    issue_v(vr);
                 __builtin_amdgcn_sched_barrier(0);
                 // One tile; PF: also request the next one (every tile but the segment's last).
                 auto step = [&](const int32_t t, auto pf_tag) {
@@ -506,7 +531,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     // address unit at once (measured: both at the top cost 12% on C3)
                     __builtin_amdgcn_sched_barrier(0);
                     if constexpr (MODE != kMaxScan && PF)
-                        issue(a.v_pages, vr);
+                        issue_v(vr);
                     __syncthreads();
                     __builtin_amdgcn_sched_barrier(0);
                     // (3) owners: reduce, mask, softmax, publish P^T
@@ -738,6 +763,23 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 }
             }
             __syncthreads();
+            if constexpr (APPEND) {
+                // the workgroup holding the last tile of the first row group writes the block's
+                // K/V rows of this kv-head into their page slots (each (token, kv-head) row once)
+                if (grp == 0 && t1 == g.ntiles) {
+                    const int32_t nch = D / 8;  // 16-byte chunks per row
+                    for (int32_t c = threadIdx.x; c < n * nch; c += C::THREADS) {
+                        const int32_t i = c / nch;
+                        const int32_t ch = c % nch;
+                        const int32_t p = L + i;
+                        const int64_t page = pt[p >> a.page_shift];
+                        const int64_t dst = ((page << a.page_shift) + (p & (psize - 1))) * hkvd + head_off + ch * 8;
+                        const int64_t src = (qstart + i) * (int64_t)hkvd + head_off + ch * 8;
+                        *reinterpret_cast<u32x4_t*>(a.k_dst + dst) = ldg16(a.k_new + src);
+                        *reinterpret_cast<u32x4_t*>(a.v_dst + dst) = ldg16(a.v_new + src);
+                    }
+                }
+            }
             if (!whole && a.ctr) {
                 // record the piece; it is counted in after the run (below), when its stores
                 // have long completed -- a wait for them here would stall the run
@@ -851,7 +893,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 
 // Raises a kernel's dynamic-LDS limit once per device (not on every launch: a call
 // being captured into a graph then enqueues nothing but the launch itself).
-template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG>
+template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG, bool APPEND = false>
 static hipError_t ensure_lds_limit()
 {
     using C = Cfg<DP, RT>;
@@ -865,48 +907,48 @@ static hipError_t ensure_lds_limit()
     const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
     if (bit && (done.load(std::memory_order_acquire) & bit))
         return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel<DP, RT, EXACT, SPANS, WIDEPG>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_mfma_kernel<DP, RT, EXACT, SPANS, WIDEPG, APPEND>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     if (e == hipSuccess && bit)
         done.fetch_or(bit, std::memory_order_release);
     return e;
 }
 
-template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG>
+template <int DP, int RT, bool EXACT, bool SPANS, bool WIDEPG, bool APPEND>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t stream)
 {
     using C = Cfg<DP, RT>;
-    const hipError_t e = ensure_lds_limit<DP, RT, EXACT, SPANS, WIDEPG>();
+    const hipError_t e = ensure_lds_limit<DP, RT, EXACT, SPANS, WIDEPG, APPEND>();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((attn_mfma_kernel<DP, RT, EXACT, SPANS, WIDEPG>), dim3(a.d.P), dim3(C::THREADS),
+    hipLaunchKernelGGL((attn_mfma_kernel<DP, RT, EXACT, SPANS, WIDEPG, APPEND>), dim3(a.d.P), dim3(C::THREADS),
                        C::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
-template <int DP, bool EXACT, bool SPANS, bool WIDEPG>
+template <int DP, bool EXACT, bool SPANS, bool WIDEPG, bool APPEND>
 static hipError_t launch_rt(const AttnArgs& a, int row_tiles, hipStream_t stream)
 {
     switch (row_tiles) {
-    case 1: return launch_one<DP, 1, EXACT, SPANS, WIDEPG>(a, stream);
-    case 2: return launch_one<DP, 2, EXACT, SPANS, WIDEPG>(a, stream);
-    case 3: return launch_one<DP, 3, EXACT, SPANS, WIDEPG>(a, stream);
-    case 4: return launch_one<DP, 4, EXACT, SPANS, WIDEPG>(a, stream);
-    case 5: return launch_one<DP, 5, EXACT, SPANS, WIDEPG>(a, stream);
+    case 1: return launch_one<DP, 1, EXACT, SPANS, WIDEPG, APPEND>(a, stream);
+    case 2: return launch_one<DP, 2, EXACT, SPANS, WIDEPG, APPEND>(a, stream);
+    case 3: return launch_one<DP, 3, EXACT, SPANS, WIDEPG, APPEND>(a, stream);
+    case 4: return launch_one<DP, 4, EXACT, SPANS, WIDEPG, APPEND>(a, stream);
+    case 5: return launch_one<DP, 5, EXACT, SPANS, WIDEPG, APPEND>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <bool SPANS, bool WIDEPG>
+template <bool SPANS, bool WIDEPG, bool APPEND = false>
 static hipError_t launch_dp(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream)
 {
     switch (dpad) {
-    case 128: return a.D == 128 ? launch_rt<128, true, SPANS, WIDEPG>(a, row_tiles, stream)
-                                : launch_rt<128, false, SPANS, WIDEPG>(a, row_tiles, stream);
-    case 256: return a.D == 256 ? launch_rt<256, true, SPANS, WIDEPG>(a, row_tiles, stream)
-                                : launch_rt<256, false, SPANS, WIDEPG>(a, row_tiles, stream);
-    case 512: return a.D == 512 ? launch_rt<512, true, SPANS, WIDEPG>(a, row_tiles, stream)
-                                : launch_rt<512, false, SPANS, WIDEPG>(a, row_tiles, stream);
+    case 128: return a.D == 128 ? launch_rt<128, true, SPANS, WIDEPG, APPEND>(a, row_tiles, stream)
+                                : launch_rt<128, false, SPANS, WIDEPG, APPEND>(a, row_tiles, stream);
+    case 256: return a.D == 256 ? launch_rt<256, true, SPANS, WIDEPG, APPEND>(a, row_tiles, stream)
+                                : launch_rt<256, false, SPANS, WIDEPG, APPEND>(a, row_tiles, stream);
+    case 512: return a.D == 512 ? launch_rt<512, true, SPANS, WIDEPG, APPEND>(a, row_tiles, stream)
+                                : launch_rt<512, false, SPANS, WIDEPG, APPEND>(a, row_tiles, stream);
     default: return hipErrorInvalidValue;
     }
 }

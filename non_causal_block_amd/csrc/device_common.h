@@ -265,6 +265,15 @@ struct AttnArgs {
     // the launch and zero again after it.  nullptr: the kernel leaves the partials for
     // the combine kernel.
     uint32_t* ctr;
+    // Fused block K/V append (APPEND instances only): the block's K/V rows, bf16
+    // [total_q][Hkv][D] in request order; writable views of the pages; and the element
+    // offsets k_new - k_pages and (v_new - v_pages) - (k_new - k_pages).
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    uint16_t* k_dst;
+    uint16_t* v_dst;
+    int64_t app_dk;
+    int64_t app_dv;
     Decomp d;
     int32_t Hq;
     int32_t D;         // real head_dim

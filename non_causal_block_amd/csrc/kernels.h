@@ -18,6 +18,8 @@ int ref_wgs_per_cu();  // resident workgroups per CU on the current device (0 if
 hipError_t launch_attn_mfma(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
 // the same with bidirectional spans (a.span_offsets non-null); attn_mfma_spans.hip
 hipError_t launch_attn_mfma_spans(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
+// the same with the block K/V append fused in (pages of >= 16 keys, no spans); attn_mfma_append.hip
+hipError_t launch_attn_mfma_append(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
 // the same for pages of fewer than 16 keys (a.page_shift < 4); attn_mfma_small_pages.hip
 hipError_t launch_attn_mfma_small_pages(const AttnArgs& a, int dpad, int row_tiles, hipStream_t stream);
 int mfma_tile_keys();

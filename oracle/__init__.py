@@ -34,6 +34,11 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def is_built() -> bool:
+    """The compiled library exists and is newer than its source."""
+    return os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC)
+
+
 def bind(path: str):
     """Load a compiled oracle library and declare its signature."""
     lib = ctypes.CDLL(path)

@@ -4,9 +4,12 @@
   equal the oracle's append, bit for bit (every other slot keeps its poison).
 * dflash_block_attn_append on context-only pages equals the fp64 oracle's
   attention over the full workload (same tolerances as every parity test).
-* The whole call captured into a HIP graph (torch.cuda.CUDAGraph) replays
-  correctly: three replays, each after eager work that restores the
-  context-only pages and clears the output, each bit-identical to the eager call.
+* The whole call captured into a HIP graph (torch.cuda.CUDAGraph) at each
+  block-aligned capture size (9, 18, 36, 72 query tokens) replays correctly: three
+  replays, each after eager work that restores the context-only pages and clears
+  the output, each bit-identical to the eager call.
+* Where the append is fused into the attention launch (MFMA kernel, pages of >= 16
+  keys), output and pages equal those of the two separate calls, bit for bit.
 """
 import numpy as np
 import pytest
@@ -90,8 +93,25 @@ def test_attn_append_matches_oracle(case):
     assert_parity(to_f64(t["out"]), oracle.run_workload(wl), f"append case {case}")
 
 
-def test_graph_capture_replays_match_eager():
-    wl, k_new, v_new, kc, vc = _setup(1)
+def _draft_step(shape: str, B: int):
+    """A draft step at a block-aligned capture size: B requests x block 9 (9, 18, 36 or 72
+    query tokens), request shapes of the C1 (head_dim 128) and C2 (head_dim 256) workloads."""
+    rng = np.random.default_rng(2000 + B)
+    if shape == "c1":
+        Hq, Hkv, D, ctx = 8, 2, 128, np.full(B, 512)
+    else:
+        Hq, Hkv, D, ctx = 32, 8, 256, rng.integers(1024, 4097, size=B)
+    wl = workloads.build(B, Hq, Hkv, D, ctx, np.full(B, 9), np.zeros(B, dtype=np.uint8), seed=2100 + B)
+    return (wl, *workloads.split_block_kv(wl))
+
+
+@pytest.mark.parametrize("shape", ["c1", "c2"])
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_graph_capture_replays_match_eager(shape, B):
+    """The whole draft step captured into a HIP graph at each capture size replays
+    bit-identically to the eager call, three times, with eager work (pages restored,
+    output cleared) and synchronisations between the replays."""
+    wl, k_new, v_new, kc, vc = _draft_step(shape, B)
     t = _inputs(wl, k_new, v_new, kc, vc)
     kc_dev, vc_dev = t["kp"].clone(), t["vp"].clone()
     desc, ws = _desc(wl)
@@ -100,8 +120,9 @@ def test_graph_capture_replays_match_eager():
     with torch.cuda.stream(side):
         assert _attn_append(wl, t, desc, side.cuda_stream) == nb.DFLASH_OK
     torch.cuda.synchronize()
-    out_eager, kp_eager = t["out"].clone(), t["kp"].clone()
+    out_eager, kp_eager, vp_eager = t["out"].clone(), t["kp"].clone(), t["vp"].clone()
     assert_parity(to_f64(out_eager), oracle.run_workload(wl), "eager")
+    assert np.array_equal(_bits(kp_eager), wl.k_pages) and np.array_equal(_bits(vp_eager), wl.v_pages)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
@@ -116,3 +137,27 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(t["out"].view(torch.int16), out_eager.view(torch.int16)), f"replay {rep}"
         assert torch.equal(t["kp"].view(torch.int16), kp_eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(t["vp"].view(torch.int16), vp_eager.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_fused_append_equals_append_then_attention(case):
+    """dflash_block_attn_append (one launch where the append is fused) against the two
+    separate calls on the same inputs: the same output and the same pages, bit for bit."""
+    wl, k_new, v_new, kc, vc = _setup(case)
+    stream = torch.cuda.current_stream().cuda_stream
+    t1 = _inputs(wl, k_new, v_new, kc, vc)
+    desc, _ = _desc(wl)
+    assert _attn_append(wl, t1, desc, stream) == nb.DFLASH_OK, nb.dflash_last_error_message()
+    t2 = _inputs(wl, k_new, v_new, kc, vc)
+    desc2, _ = _desc(wl)
+    st = nb.dflash_block_kv_append(t2["kn"], t2["vn"], t2["kp"], t2["vp"], t2["pt"], t2["ctx"], t2["blk"], wl.Hkv,
+                                   wl.D, stream, desc2)
+    assert st == nb.DFLASH_OK, nb.dflash_last_error_message()
+    st = nb.dflash_block_attn(t2["q"], t2["kp"], t2["vp"], t2["pt"], t2["ctx"], t2["blk"], wl.Hq, wl.Hkv, wl.D,
+                              t2["causal"], wl.window, wl.scale, t2["out"], stream, desc2)
+    assert st == nb.DFLASH_OK, nb.dflash_last_error_message()
+    torch.cuda.synchronize()
+    assert torch.equal(t1["out"].view(torch.int16), t2["out"].view(torch.int16))
+    assert torch.equal(t1["kp"].view(torch.int16), t2["kp"].view(torch.int16))
+    assert torch.equal(t1["vp"].view(torch.int16), t2["vp"].view(torch.int16))
