@@ -379,6 +379,7 @@ def conv_bench(reps: int = 200) -> dict:
         stream = torch.cuda.current_stream(dev)
         for _ in range(10):
             nb.block_conv(tx, tb, td, bl, groups=G, out=out)
+        # one call alone between two events: includes the launch reaching an idle GPU
         e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         for i in range(reps):
@@ -386,14 +387,54 @@ def conv_bench(reps: int = 200) -> dict:
             nb.block_conv(tx, tb, td, bl, groups=G, out=out)
             e1[i].record(stream)
         torch.cuda.synchronize()
-        us = float(np.median([e0[i].elapsed_time(e1[i]) * 1e3 for i in range(reps)]))
+        call_us = float(np.median([e0[i].elapsed_time(e1[i]) * 1e3 for i in range(reps)]))
+        # calls back to back (the host runs ahead): GPU time per call in a stream of them
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(reps):
+            nb.block_conv(tx, tb, td, bl, groups=G, out=out)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        b2b_us = b0.elapsed_time(b1) * 1e3 / reps
+        # 20 calls captured in one HIP graph, replayed: GPU time per call without the host's
+        # launch cost (a Python call here costs more host time than the kernel takes)
+        per_graph, replays = 20, 20
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            nb.block_conv(tx, tb, td, bl, groups=G, out=out)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                nb.block_conv(tx, tb, td, bl, groups=G, out=out)
+        g.replay()
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        us = b0.elapsed_time(b1) * 1e3 / (replays * per_graph)
         nbytes = (x.size + out.numel() + base.size + delta.size) * 2
         res.append({"B": B, "block": 16, "channels": C, "groups": G, "taps": taps, "gpu_us": us,
-                    "algorithmic_bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
-                    "positions_per_s": B * 16 / (us * 1e-6)})
-        print(f"[conv] B={B}: {us:.1f} us, {nbytes/1e6:.1f} MB -> {nbytes/(us*1e-6)/1e9:.0f} GB/s",
+                    "back_to_back_us": b2b_us, "call_us": call_us, "algorithmic_bytes": nbytes,
+                    "gbps": nbytes / (us * 1e-6) / 1e9, "positions_per_s": B * 16 / (us * 1e-6)})
+        print(f"[conv] B={B}: {us:.1f} us per call in a graph of {per_graph} ({b2b_us:.1f} us back to back, "
+              f"{call_us:.1f} us alone), {nbytes/1e6:.1f} MB -> {nbytes/(us*1e-6)/1e9:.0f} GB/s",
               file=sys.stderr, flush=True)
-    return {"metric": "DFlash2 in-block grouped dynamic depthwise convolution, GPU us per call (median)",
+    # known-size traffic for scaling FETCH_SIZE / WRITE_SIZE in counter runs of this mode:
+    # one fill of 256 MiB (a write) and one streaming read of it
+    cal_bytes = 256 << 20
+    cal = torch.empty(cal_bytes // 4, dtype=torch.float32, device=dev)
+    cal.fill_(1.0)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = nb.dflash_stream_read(cal, cal_bytes, sink, stream.cuda_stream)
+    if st != nb.DFLASH_OK:
+        raise RuntimeError(f"stream_read failed: {nb.dflash_last_error_message()}")
+    torch.cuda.synchronize()
+    return {"metric": "DFlash2 in-block grouped dynamic depthwise convolution, GPU us per call (20 calls per replayed graph)",
             "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": res}
 
 

@@ -26,6 +26,12 @@ CASES = [
     ([16, 7], 64, 4, 20),          # more taps than positions
     ([1], 2, 1, 1),
     ([4, 15, 8, 2, 16, 11], 1024, 16, 8),
+    ([40, 17, 3, 33], 512, 8, 16),   # blocks longer than the 16-position chunks of the tiled kernel
+    ([9, 33], 256, 128, 8),          # more groups than the tiled kernel stages: the per-position kernel
+    ([16] * 64, 5120, 32, 16),       # the benchmark's shape (64 requests x 16 positions)
+    ([20, 35, 16], 1024, 16, 3),     # odd tap count, two tap pairs, later chunks
+    ([18, 5, 0, 31], 768, 12, 7),    # four tap pairs, 64 channels per group
+    ([16, 2], 1536, 3, 16),          # 512 channels per group: a workgroup inside one group
 ]
 
 
