@@ -33,3 +33,25 @@ def pytest_sessionfinish(session, exitstatus):
     from tests import native_builds
 
     native_builds.cleanup()
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The full-size parity table of this session (GPU runs only)."""
+    helpers = sys.modules.get("tests.gpu_helpers")
+    rows = getattr(helpers, "PARITY_REPORT", None)
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.write_line("")
+    tr.write_line("full-size parity against the fp64 oracle (every output element):")
+    tr.write_line("| workload | kernel | rows | max abs err | mean abs err | rel RMS err | oracle s |")
+    tr.write_line("|---|---|---|---|---|---|---|")
+    for r in rows:
+        tr.write_line(f"| {r['workload']} | {r['kernel']} | {r['rows']} | {r['max_abs']:.2e} | {r['mean_abs']:.2e} | "
+                      f"{r['rel_rms']:.2e} | {r['oracle_s']:.2f} |")
+    path = os.environ.get("DFLASH_PARITY_REPORT")
+    if path:
+        import json
+
+        with open(path, "w") as f:
+            json.dump(rows, f, indent=1)

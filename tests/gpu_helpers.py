@@ -67,6 +67,16 @@ def metrics(got: np.ndarray, ref: np.ndarray) -> dict:
                 finite=bool(np.isfinite(got).all()))
 
 
+# Full-size parity results of this session (workload, kernel, metrics, oracle wall time),
+# printed as a table at the end of the run (conftest.py) and written as JSON to the file
+# named by DFLASH_PARITY_REPORT when that is set.
+PARITY_REPORT: list = []
+
+
+def record(workload: str, kernel: str, m: dict, oracle_s: float, rows: int) -> None:
+    PARITY_REPORT.append(dict(workload=workload, kernel=kernel, rows=rows, oracle_s=oracle_s, **m))
+
+
 def assert_parity(got: np.ndarray, ref: np.ndarray, what: str = ""):
     m = metrics(got, ref)
     assert m["finite"], f"{what}: non-finite output"

@@ -4,6 +4,8 @@ Every call goes through the C ABI (non_causal_block_amd -> libdflash_attn.so).
 Tolerances: max|err| <= 2e-2 and mean|err| <= 2e-3 on bf16 outputs, plus a
 relative RMS error <= 1e-2 (tests/gpu_helpers.py).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -26,11 +28,21 @@ def _gpu():
     # the oracle library was compiled at session start, before the GPU was touched
 
 
-def _full(name, kernel, **kw):
+KNAMES = {nb.DFLASH_KERNEL_AUTO: "auto", nb.DFLASH_KERNEL_MFMA: "mfma", nb.DFLASH_KERNEL_REFERENCE: "ref"}
+
+
+def _full(name, kernel, report=True, **kw):
+    """Every output element of the workload against the oracle; full-size runs go into the
+    session's parity report."""
     wl = workloads.make(name, **kw)
+    t0 = time.perf_counter()
     ref = oracle.run_workload(wl)
+    oracle_s = time.perf_counter() - t0
     got = H.to_f64(H.run(wl, kernel=kernel))
-    return H.assert_parity(got, ref, f"{name} kernel={kernel}")
+    m = H.assert_parity(got, ref, f"{name} kernel={kernel}")
+    if report:
+        H.record(name, KNAMES.get(kernel, str(kernel)), m, oracle_s, int(ref.shape[0] * ref.shape[1]))
+    return m
 
 
 # ---------------------------------------------------------------------------
@@ -58,7 +70,7 @@ def test_c4_causal_window_d256(kname, kernel):
 
 @pytest.mark.parametrize("kname,kernel", KERNELS)
 def test_c5_mixed_d512_reduced(kname, kernel):
-    _full("c5_mixed_d512", kernel, ctx_cap=1500)
+    _full("c5_mixed_d512", kernel, report=False, ctx_cap=1500)
 
 
 # target-side verification on a hybrid model: local sliding-window and global layers
@@ -74,9 +86,7 @@ def test_c5_mixed_d512_full_every_row():
     """The full-size mixed batch (B = 64, lognormal contexts up to 131072 keys) in the
     benchmark's launch configuration, every output element against the fp64 oracle
     (about 9 s of oracle time on 16 host threads)."""
-    wl = workloads.make("c5_mixed_d512")
-    got = H.to_f64(H.run(wl))
-    H.assert_parity(got, oracle.run_workload(wl), "c5 full, every row")
+    _full("c5_mixed_d512", nb.DFLASH_KERNEL_AUTO)
 
 
 # ---------------------------------------------------------------------------
