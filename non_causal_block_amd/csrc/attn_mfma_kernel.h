@@ -198,6 +198,7 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     constexpr int DT = C::DT;
     constexpr int DW = C::DW;
     constexpr int NOWN = C::NOWN;
+    constexpr bool LATE_V = DP <= 256;  // where V is staged and requested (see the tile step)
 
     if (a.dbg && *a.dbg != 0u)
         return;  // debug checks found a bad device-side value: touch nothing
@@ -466,9 +467,17 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     }
                 };
 
-                // One 32-key tile per step.  At the top of step t the registers holding the
-                // K/V of tile t are written to LDS and at once refilled with tile t+1, which
-                // so has a whole step to arrive.  Inside the loop every request is
+                // One 32-key tile per step.  At the top of step t the registers holding K of
+                // tile t are written to LDS and at once refilled with K of tile t+1, which so
+                // has a whole step to arrive.  V is requested apart from K, so that the two
+                // halves of the workgroup's 64 KB do not queue at the address unit at once
+                // (both at the top measured 12% slower on C3).  Up to head_dim 256 (LATE_V)
+                // V(t) goes to LDS just before the PV product and V(t+1) is requested there,
+                // so V too has a whole step and waiting for K(t) never waits for V(t)
+                // (C2 40.4 vs 42.5 us, A/B on one box).  At head_dim 512, V(t) goes to LDS
+                // with K(t) and V(t+1) is requested after the S^T product: the late form
+                // keeps V's registers live across that product, and measured 1-2% slower
+                // (C5, the global verify layer) with C3 unchanged.  Inside the loop every request is
                 // unconditional (keys past the request read its last key, page entries are
                 // read at clamped indices): the loop has no divergent branches and each wait
                 // on the memory counter is exact.  The issue order (page entries, K, V) is pinned with
@@ -486,10 +495,11 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 auto step = [&](const int32_t t, auto pf_tag) {
                     constexpr bool PF = decltype(pf_tag)::value;
                     const int32_t k0 = g.kv_lo + t * kTK;
-                    // (1) this wave's K and V slices -> LDS [key][d_local].  Keys past the
-                    // request hold its last key and d past head_dim the row start: finite
-                    // values whose weight (masked logit) or output column (never stored) is 0.
-                    if constexpr (MODE != kMaxScan) {
+                    // (1) this wave's K slice (and, unless LATE_V, its V slice) -> LDS
+                    // [key][d_local].  Keys past the request hold its last key and d past
+                    // head_dim the row start: finite values whose weight (masked logit) or
+                    // output column (never stored) is 0.
+                    if constexpr (MODE != kMaxScan && !LATE_V) {
 #pragma unroll
                         for (int i = 0; i < NI; ++i)
                             *reinterpret_cast<u32x4_t*>(vls + C::vofs(i * KPI + kl, 2 * sl)) = vr[i];
@@ -509,29 +519,49 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                     // (2) partial S^T over this wave's d-slice (absent d: Q is zero there and K
                     //     finite; absent keys are masked below).  A operand: key 16h + l16,
                     //     d chunk 4s + grp4 of the slice.
-                    bf16x8_t kb[2][KS];
+                    if constexpr (LATE_V) {
+                        // one 16-key half at a time: V(t)'s registers are live here
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                        for (int h = 0; h < 2; ++h) {
+                            bf16x8_t kb[KS];
 #pragma unroll
-                        for (int s = 0; s < KS; ++s)
-                            kb[h][s] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kls + C::kofs(16 * h + l16, 4 * s + grp4)));
+                            for (int s = 0; s < KS; ++s)
+                                kb[s] = as_bf16x8(
+                                    *reinterpret_cast<const u32x4_t*>(kls + C::kofs(16 * h + l16, 4 * s + grp4)));
 #pragma unroll
-                    for (int b = 0; b < RT; ++b) {
-                        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+                            for (int b = 0; b < RT; ++b) {
+                                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int s = 0; s < KS; ++s) {
-                            acc0 = mfma16(kb[0][s], qf[b][s], acc0);
-                            acc1 = mfma16(kb[1][s], qf[b][s], acc1);
+                                for (int s = 0; s < KS; ++s)
+                                    acc = mfma16(kb[s], qf[b][s], acc);
+                                sx[((wave * 2 + h) * RT + b) * 64 + lane] = acc;
+                            }
                         }
-                        sx[((wave * 2 + 0) * RT + b) * 64 + lane] = acc0;
-                        sx[((wave * 2 + 1) * RT + b) * 64 + lane] = acc1;
+                    } else {
+                        bf16x8_t kb[2][KS];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int s = 0; s < KS; ++s)
+                                kb[h][s] = as_bf16x8(
+                                    *reinterpret_cast<const u32x4_t*>(kls + C::kofs(16 * h + l16, 4 * s + grp4)));
+#pragma unroll
+                        for (int b = 0; b < RT; ++b) {
+                            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s = 0; s < KS; ++s) {
+                                acc0 = mfma16(kb[0][s], qf[b][s], acc0);
+                                acc1 = mfma16(kb[1][s], qf[b][s], acc1);
+                            }
+                            sx[((wave * 2 + 0) * RT + b) * 64 + lane] = acc0;
+                            sx[((wave * 2 + 1) * RT + b) * 64 + lane] = acc1;
+                        }
+                        // V of tile t+1, requested after this wave's products
+                        __builtin_amdgcn_sched_barrier(0);
+                        if constexpr (MODE != kMaxScan && PF)
+                            issue_v(vr);
                     }
-                    // V of tile t+1: requested after this wave's products rather than with K,
-                    // so that the two halves of the workgroup's 64 KB do not queue at the
-                    // address unit at once (measured: both at the top cost 12% on C3)
                     __builtin_amdgcn_sched_barrier(0);
-                    if constexpr (MODE != kMaxScan && PF)
-                        issue_v(vr);
                     __syncthreads();
                     __builtin_amdgcn_sched_barrier(0);
                     // (3) owners: reduce, mask, softmax, publish P^T
@@ -624,7 +654,18 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                             anyover |= flag_s[b];
                         aborted = __builtin_amdgcn_readfirstlane(anyover) != 0;
                     }
-                    // (4) O^T += V^T P^T for this wave's d-slice
+                    // (4) LATE_V: this wave's V slice of tile t -> LDS (the wave's own tile: no
+                    // barrier), and V of tile t+1 requested into the freed registers
+                    if constexpr (LATE_V) {
+#pragma unroll
+                        for (int i = 0; i < NI; ++i)
+                            *reinterpret_cast<u32x4_t*>(vls + C::vofs(i * KPI + kl, 2 * sl)) = vr[i];
+                        __builtin_amdgcn_sched_barrier(0);
+                        if constexpr (PF)
+                            issue_v(vr);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    // (5) O^T += V^T P^T for this wave's d-slice
                     // A operand V^T: lane l holds d = 16c + l%16 at key slots 4*grp4 + 0..3
                     // and 16 + 4*grp4 + 0..3 (the key order of P^T).  Transposing reads:
                     // lane j of group grp4 addresses key 4*grp4 + j/4 (and +16) at
