@@ -629,11 +629,14 @@ def main(argv=None) -> int:
         },
         "kv_hbm_gbps": call_gbps,
         "kv_hbm_frac_of_peak": call_gbps / HBM_PEAK_GBPS,
+        "kv_hbm_basis": "whole dflash_block_attn call (attention + split-KV combine), mean over the timed calls",
         "stream_read_gbps": stream_gbps,
         "attn_kv_frac_of_stream_read": achieved / stream_gbps,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "basis": "attention kernel alone: mean of HIP events around it on its launch stream",
+            "call_frac": call_gbps / HBM_PEAK_GBPS,
             "kernel": "attn_mfma_kernel" if plan.kernel == nb.DFLASH_KERNEL_MFMA else "attn_ref_kernel",
             "kernel_sha": khash,
         },
