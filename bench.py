@@ -80,8 +80,9 @@ def visible_kv_bytes(wl) -> int:
     return int(U.sum()) * wl.Hkv * wl.D * 2 * 2
 
 
-def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle (unchanged) on a bounded sample of the workload's rows."""
+def cpu_baseline(wl, budget_s: float = 12.0, spans=None) -> dict:
+    """The fp64 oracle (unchanged) on a bounded sample of the workload's rows (with the
+    call's bidirectional spans, if any)."""
     import numpy as np
 
     import oracle
@@ -96,18 +97,18 @@ def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
     # calibrate on a few rows, then size the sample for ~budget_s of work
     probe = rng.choice(all_rows, size=min(all_rows, max(threads, 8)), replace=False)
     t0 = time.perf_counter()
-    oracle.run_workload(wl, rows=probe, threads=threads)
+    oracle.run_workload(wl, rows=probe, threads=threads, spans=spans)
     dt = max(time.perf_counter() - t0, 1e-4)
     per_row = dt / len(probe)
     n_rows = int(min(all_rows, max(len(probe), budget_s / per_row)))
     rows = np.sort(rng.choice(all_rows, size=n_rows, replace=False))
     t0 = time.perf_counter()
-    oracle.run_workload(wl, rows=rows, threads=threads)
+    oracle.run_workload(wl, rows=rows, threads=threads, spans=spans)
     dt = time.perf_counter() - t0
     tokens = n_rows / wl.Hq  # one query token = Hq output rows
     return {"value": tokens / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_rows} of {all_rows} (token, q-head) output rows drawn uniformly from {wl.name}, "
-                      f"fp64, {dt:.1f} s on {threads} threads"}
+            "sample": f"{n_rows} of {all_rows} (token, q-head) output rows drawn uniformly from {wl.name}"
+                      f"{' with its spans' if spans is not None else ''}, fp64, {dt:.1f} s on {threads} threads"}
 
 
 def traffic_for(kernel_hash: str, launches_bytes: float):
@@ -352,7 +353,7 @@ def graph_latency(reps: int = 200, only: str = "") -> dict:
             "control": control}
 
 
-def conv_bench(reps: int = 200) -> dict:
+def conv_bench(reps: int = 200, cpu_baseline_leg: bool = True) -> dict:
     """DFlash2 block convolution: GPU time per call and algorithmic bytes per second.
 
     Shapes are readings (the pages give the formula, not the model sizes): blocks
@@ -418,9 +419,27 @@ def conv_bench(reps: int = 200) -> dict:
         torch.cuda.synchronize()
         us = b0.elapsed_time(b1) * 1e3 / (replays * per_graph)
         nbytes = (x.size + out.numel() + base.size + delta.size) * 2
-        res.append({"B": B, "block": 16, "channels": C, "groups": G, "taps": taps, "gpu_us": us,
-                    "back_to_back_us": b2b_us, "call_us": call_us, "algorithmic_bytes": nbytes,
-                    "gbps": nbytes / (us * 1e-6) / 1e9, "positions_per_s": B * 16 / (us * 1e-6)})
+        gbps = nbytes / (us * 1e-6) / 1e9
+        row = {"B": B, "block": 16, "channels": C, "groups": G, "taps": taps, "gpu_us": us,
+               "back_to_back_us": b2b_us, "call_us": call_us, "algorithmic_bytes": nbytes, "gbps": gbps,
+               "positions_per_s": B * 16 / (us * 1e-6),
+               "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": gbps / HBM_PEAK_GBPS,
+                            "basis": "algorithmic bytes (x, out, base, delta once) / GPU time per call in a "
+                                     "replayed graph of 20 calls"}}
+        if cpu_baseline_leg:
+            # the sequential fp64 oracle on the same inputs (every position of the batch)
+            from oracle.block_conv import block_conv_f64
+
+            f = lambda a: (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+            xf, bf, df = f(x), f(base), f(delta)
+            t0 = time.perf_counter()
+            block_conv_f64(xf, bf, df, blocks, G)
+            dt = time.perf_counter() - t0
+            row["cpu_baseline"] = {"value": B * 16 / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+                                   "sample": f"all {B * 16} positions of the {B}-request batch, fp64 numpy, "
+                                             f"{dt:.2f} s on one thread"}
+        res.append(row)
         print(f"[conv] B={B}: {us:.1f} us per call in a graph of {per_graph} ({b2b_us:.1f} us back to back, "
               f"{call_us:.1f} us alone), {nbytes/1e6:.1f} MB -> {nbytes/(us*1e-6)/1e9:.0f} GB/s",
               file=sys.stderr, flush=True)
@@ -456,6 +475,8 @@ def main(argv=None) -> int:
     ap.add_argument("--graph-shape", default="", help="with --graph-latency: only this shape, e.g. c1:1")
     ap.add_argument("--graph-reps", type=int, default=200)
     ap.add_argument("--conv", action="store_true")
+    ap.add_argument("--spans", action="store_true",
+                    help="call dflash_block_attn_spans with seeded bidirectional spans (causal requests)")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
@@ -492,8 +513,8 @@ def main(argv=None) -> int:
 
     if args.graph_latency or args.conv:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
-        print(json.dumps(graph_latency(args.graph_reps, args.graph_shape) if args.graph_latency else conv_bench()),
-              flush=True)
+        print(json.dumps(graph_latency(args.graph_reps, args.graph_shape) if args.graph_latency
+                         else conv_bench(cpu_baseline_leg=not args.no_cpu_baseline)), flush=True)
         return 0
 
     if not os.path.exists(nb._lib.LIB_PATH):
@@ -511,6 +532,16 @@ def main(argv=None) -> int:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, kp, vp = t16(wl.q), t16(wl.k_pages), t16(wl.v_pages)
+    span_offs = span_tab = None
+    n_spans = 0
+    if args.spans:
+        lists = workloads.draw_spans(wl.ctx_lens, wl.block_lens, seed=wl.seed + 7)
+        offs = np.zeros(wl.B + 1, dtype=np.int32)
+        offs[1:] = np.cumsum([len(x) for x in lists])
+        flat = np.asarray([p for x in lists for p in x], dtype=np.int32).reshape(-1, 2)
+        n_spans = int(flat.shape[0])
+        span_offs = torch.from_numpy(offs).to(dev)
+        span_tab = torch.from_numpy(np.ascontiguousarray(flat)).to(dev) if n_spans else None
     pt = torch.from_numpy(wl.page_table).to(dev)
     ctx = torch.from_numpy(wl.ctx_lens).to(dev)
     blk = torch.from_numpy(wl.block_lens).to(dev)
@@ -554,8 +585,12 @@ def main(argv=None) -> int:
         else:
             desc.event_attn_begin, desc.event_attn_end = None, None
             call0[i].record(stream)
-        st = nb.dflash_block_attn(q, kp, vp, pt, ctx, blk, wl.Hq, wl.Hkv, wl.D, causal, wl.window, wl.scale, out,
-                                  stream.cuda_stream, desc)
+        if args.spans:
+            st = nb.dflash_block_attn_spans(q, kp, vp, pt, ctx, blk, wl.Hq, wl.Hkv, wl.D, causal, span_offs,
+                                            span_tab, n_spans, wl.window, wl.scale, out, stream.cuda_stream, desc)
+        else:
+            st = nb.dflash_block_attn(q, kp, vp, pt, ctx, blk, wl.Hq, wl.Hkv, wl.D, causal, wl.window, wl.scale,
+                                      out, stream.cuda_stream, desc)
         if not instrumented:
             call1[i].record(stream)
         if st != nb.DFLASH_OK:
@@ -605,7 +640,7 @@ def main(argv=None) -> int:
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl)
+        cpu = cpu_baseline(wl, spans=lists if args.spans else None)
 
     cfg = workloads.CONFIGS[args.config]
     line = {
@@ -626,6 +661,7 @@ def main(argv=None) -> int:
             "head_dim": wl.D, "query_tokens": tokens, "total_kv_tokens": wl.total_kv, "window": wl.window,
             "page_size": wl.page_size, "seed": wl.seed, "kernel": args.kernel,
             "attn_workgroups": plan.num_workgroups, "kv_bytes": kv_bytes,
+            **({"spans": n_spans} if args.spans else {}),
         },
         "kv_hbm_gbps": call_gbps,
         "kv_hbm_frac_of_peak": call_gbps / HBM_PEAK_GBPS,
