@@ -80,6 +80,18 @@ def visible_kv_bytes(wl) -> int:
     return int(U.sum()) * wl.Hkv * wl.D * 2 * 2
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s: float = 12.0, spans=None) -> dict:
     """The fp64 oracle (unchanged) on a bounded sample of the workload's rows (with the
     call's bidirectional spans, if any)."""
@@ -106,7 +118,7 @@ def cpu_baseline(wl, budget_s: float = 12.0, spans=None) -> dict:
     oracle.run_workload(wl, rows=rows, threads=threads, spans=spans)
     dt = time.perf_counter() - t0
     tokens = n_rows / wl.Hq  # one query token = Hq output rows
-    return {"value": tokens / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tokens / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n_rows} of {all_rows} (token, q-head) output rows drawn uniformly from {wl.name}"
                       f"{' with its spans' if spans is not None else ''}, fp64, {dt:.1f} s on {threads} threads"}
 
