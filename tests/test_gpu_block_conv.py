@@ -32,6 +32,8 @@ CASES = [
     ([20, 35, 16], 1024, 16, 3),     # odd tap count, two tap pairs, later chunks
     ([18, 5, 0, 31], 768, 12, 7),    # four tap pairs, 64 channels per group
     ([16, 2], 1536, 3, 16),          # 512 channels per group: a workgroup inside one group
+    ([16, 5], 5120, 128, 16),        # 128 groups of 40 channels: a workgroup stages 14 of them
+    ([12, 16], 64, 32, 6),           # 2 channels per group: one workgroup stages all 32 groups
 ]
 
 
