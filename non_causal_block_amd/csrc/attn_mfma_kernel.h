@@ -17,9 +17,12 @@
 //    all (request, kv-head, row group) units; all G q-heads of a kv-head and
 //    all n block queries share every K/V byte (rows = n*G, tiled by 16).
 //  * The head dimension is split over the 4 waves (DW = Dp/4 each).  Wave w
-//    streams only its d-slice of every key: K straight from HBM into MFMA
-//    A-operand registers (8 consecutive d of one key per lane, 16-byte loads),
-//    V into registers and from there into a wave-private LDS tile.
+//    streams only its d-slice of every key, 16 bytes per lane so that one load
+//    covers whole slices of several keys, into registers one tile ahead, and
+//    from there into wave-private LDS tiles (K swizzled for the MFMA-order
+//    reads, V for the transposing reads).  V is requested apart from K; up to
+//    head_dim 256 it is also staged just before the PV product, so that each
+//    half of the next tile has a whole step to arrive.
 //  * S^T = K Q^T per wave over its d-slice with v_mfma_f32_16x16x32_bf16
 //    (A = K, rows = keys; B = Q^T, held for the whole unit); the four partial
 //    S^T tiles are summed through LDS by the wave that owns the row tile, which
