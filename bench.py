@@ -56,6 +56,7 @@ METRIC = "query-tokens/s + K/V HBM GB/s (% of peak) for block attention, 1 MI355
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_mfma_c3_global_d512.json")
 FLUSH_BYTES = 1 << 30
+SETTLE_STEPS = 25  # untimed steps (warm-up included) before the timed ones
 KERNEL_SOURCES = ["attn_mfma_kernel.h", "attn_mfma.hip", "device_common.h", "decomp.h", "merge.h"]
 
 
@@ -475,8 +476,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=30)
     # The attention kernel runs slower for the first ~30 flushed calls of a process on these
     # GPUs (a transient: C3 132-140 us per call, then 121-124 us from about call 40 on), so
-    # the default warm-up (two calls per step) runs past it.
-    ap.add_argument("--warmup", type=int, default=25)
+    # the default warm-up (two calls per step) runs past it; with fewer warm-up steps the
+    # bench adds untimed settle steps up to SETTLE_STEPS and reports them.
+    ap.add_argument("--warmup", type=int, default=SETTLE_STEPS)
     ap.add_argument("--config", default="c3_global_d512")
     ap.add_argument("--kernel", choices=["auto", "mfma", "ref"], default="auto")
     ap.add_argument("--num-workgroups", type=int, default=0)
@@ -614,6 +616,10 @@ def main(argv=None) -> int:
     print(f"[bench] plan: kernel={plan.kernel} workgroups={plan.num_workgroups} rows/unit={plan.rows_per_unit} "
           f"merge_in_kernel={plan.merge_in_kernel} combine={plan.combine_workgroups} "
           f"workspace={plan.workspace_bytes}", file=sys.stderr, flush=True)
+    settle = max(0, SETTLE_STEPS - args.warmup)
+    for _ in range(settle):  # untimed, past the GPU's slow first calls (see --warmup)
+        step(0, False)
+        step(0, True)
     for i in range(args.warmup):
         step(i, False)
         step(i, True)
@@ -665,6 +671,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": float(call_ms.mean()),
         "higher_is_better": True,
         "scaling": "weak",
