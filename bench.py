@@ -254,14 +254,17 @@ def _graph_node_types(graph) -> list:
     return out
 
 
-def graph_latency(reps: int = 200, only: str = "") -> dict:
-    """Per-call latency of dflash_block_attn_append, eager vs graph replay.
+def graph_latency(reps: int = 200, only: str = "", layers: int = 1) -> dict:
+    """Per-step latency of dflash_block_attn_append, eager vs graph replay.
 
-    Each call is timed alone from the host (launch to completion, warm caches:
-    a draft step re-reads the context it just read) and on the GPU (events).  The
-    captured graph's node types are listed, and a control -- one trivial torch
-    kernel, eager vs replayed graph -- measures what a graph replay costs on this
-    runtime by itself.  ``only`` ("c1:1", ...) restricts the shapes."""
+    A step is ``layers`` consecutive calls (one per layer of a draft model; the
+    same buffers serve every layer), made one by one from Python or captured
+    together as one graph.  Each step is timed alone from the host (launch to
+    completion, warm caches: a draft step re-reads the context it just read) and
+    on the GPU (events).  The captured graph's node types are listed, and a
+    control -- one trivial torch kernel, eager vs replayed graph -- measures what
+    a graph replay costs on this runtime by itself.  ``only`` ("c1:1", ...)
+    restricts the shapes."""
     import numpy as np
     import torch
 
@@ -315,11 +318,15 @@ def graph_latency(reps: int = 200, only: str = "") -> dict:
             desc.workspace, desc.workspace_bytes = ws.data_ptr(), ws.numel()
             plan = nb.dflash_block_attn_plan(desc, wl.Hq, wl.Hkv, wl.D)
 
-            def call():
+            def call_one():
                 st = nb.dflash_block_attn_append(q, kn, vn, kp, vp, pt, cl, bl, wl.Hq, wl.Hkv, wl.D, None, 0,
                                                  wl.scale, out, side.cuda_stream, desc)
                 if st != nb.DFLASH_OK:
                     raise nb.DFlashError(st, nb.dflash_last_error_message())
+
+            def call():
+                for _ in range(layers):
+                    call_one()
 
             with torch.cuda.stream(side):
                 for _ in range(10):
@@ -336,13 +343,15 @@ def graph_latency(reps: int = 200, only: str = "") -> dict:
                 torch.cuda.synchronize()
                 time.sleep(0.01)  # separates the eager calls from the replays in a kernel trace
                 graph_host, graph_gpu = timed(g.replay)
-            results.append({"shape": name, "B": B, "query_tokens": wl.total_q, "Hq": wl.Hq, "Hkv": wl.Hkv,
+            results.append({"shape": name, "B": B, "layers": layers, "query_tokens": wl.total_q, "Hq": wl.Hq,
+                            "Hkv": wl.Hkv,
                             "head_dim": wl.D, "total_kv_tokens": wl.total_kv, "attn_workgroups": plan.num_workgroups,
                             "merge_in_kernel": bool(plan.merge_in_kernel), "graph_nodes": nodes,
                             "eager_us": eager_host, "graph_us": graph_host,
                             "eager_gpu_us": eager_gpu, "graph_gpu_us": graph_gpu})
-            print(f"[graph] {name} B={B}: eager {eager_host:.1f} us (gpu {eager_gpu:.1f}), "
-                  f"graph {graph_host:.1f} us (gpu {graph_gpu:.1f}), nodes {nodes}", file=sys.stderr, flush=True)
+            print(f"[graph] {name} B={B} x {layers} layer(s): eager {eager_host:.1f} us (gpu {eager_gpu:.1f}), "
+                  f"graph {graph_host:.1f} us (gpu {graph_gpu:.1f}), nodes {nodes if layers == 1 else len(nodes)}",
+                  file=sys.stderr, flush=True)
     # control: one trivial torch kernel, eager vs replayed graph
     x = torch.zeros(16, device=dev)
     with torch.cuda.stream(side):
@@ -361,7 +370,7 @@ def graph_latency(reps: int = 200, only: str = "") -> dict:
                "graph_gpu_us": ctl_graph[1]}
     print(f"[graph] control: eager gpu {ctl_eager[1]:.1f} us, graph gpu {ctl_graph[1]:.1f} us", file=sys.stderr,
           flush=True)
-    return {"metric": "draft-step latency: block K/V append + attention, one call, us (median)",
+    return {"metric": f"draft-step latency: block K/V append + attention, {layers} call(s) per step, us (median)",
             "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "reps": reps, "results": results,
             "control": control}
 
@@ -491,6 +500,7 @@ def main(argv=None) -> int:
     ap.add_argument("--graph-latency", action="store_true")
     ap.add_argument("--graph-shape", default="", help="with --graph-latency: only this shape, e.g. c1:1")
     ap.add_argument("--graph-reps", type=int, default=200)
+    ap.add_argument("--graph-layers", type=int, default=1, help="with --graph-latency: calls per step (layers)")
     ap.add_argument("--conv", action="store_true")
     ap.add_argument("--spans", action="store_true",
                     help="call dflash_block_attn_spans with seeded bidirectional spans (causal requests)")
@@ -530,7 +540,7 @@ def main(argv=None) -> int:
 
     if args.graph_latency or args.conv:
         assert torch.cuda.is_available(), "bench.py needs a GPU"
-        print(json.dumps(graph_latency(args.graph_reps, args.graph_shape) if args.graph_latency
+        print(json.dumps(graph_latency(args.graph_reps, args.graph_shape, args.graph_layers) if args.graph_latency
                          else conv_bench(cpu_baseline_leg=not args.no_cpu_baseline)), flush=True)
         return 0
 
