@@ -522,7 +522,7 @@ def main(argv=None) -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the work shards by request / kv-head with no communication; see DESIGN.md)", file=sys.stderr)
+              "(the work shards by request / kv-head with no communication)", file=sys.stderr)
         return 2
 
     if not args.no_cpu_baseline and not (args.graph_latency or args.conv):
