@@ -202,6 +202,9 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     constexpr int DW = C::DW;
     constexpr int NOWN = C::NOWN;
     constexpr bool LATE_V = DP <= 256;  // where V is staged and requested (see the tile step)
+    // Otherwise V of the next tile is requested after this wave's S^T products, or, where a
+    // wave owns two row tiles, after the first barrier.
+    constexpr bool V_AFTER_BARRIER = !LATE_V && RT > WAVES;
 
     if (a.dbg && *a.dbg != 0u)
         return;  // debug checks found a bad device-side value: touch nothing
@@ -480,7 +483,10 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 // (C2 40.4 vs 42.5 us, A/B on one box).  At head_dim 512, V(t) goes to LDS
                 // with K(t) and V(t+1) is requested after the S^T product: the late form
                 // keeps V's registers live across that product, and measured 1-2% slower
-                // (C5, the global verify layer) with C3 unchanged.  Inside the loop every request is
+                // (C5, the global verify layer) with C3 unchanged.  With five row tiles
+                // (one wave owns two) V(t+1) goes out after the first barrier instead:
+                // C3 120.3 vs 121.7 us, the global verify layer 192.2 vs 194.6 us, while
+                // four row tiles (C5) measured 0.6% slower that way (A/B on one box).  Inside the loop every request is
                 // unconditional (keys past the request read its last key, page entries are
                 // read at clamped indices): the loop has no divergent branches and each wait
                 // on the memory counter is exact.  The issue order (page entries, K, V) is pinned with
@@ -561,12 +567,16 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                         }
                         // V of tile t+1, requested after this wave's products
                         __builtin_amdgcn_sched_barrier(0);
-                        if constexpr (MODE != kMaxScan && PF)
+                        if constexpr (MODE != kMaxScan && PF && !V_AFTER_BARRIER)
                             issue_v(vr);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     __syncthreads();
                     __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (MODE != kMaxScan && PF && V_AFTER_BARRIER) {
+                        issue_v(vr);  // ... or after the barrier
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     // (3) owners: reduce, mask, softmax, publish P^T
 #pragma unroll
                     for (int ob = 0; ob < NOWN; ++ob) {
