@@ -111,6 +111,7 @@ EDGE = [
     (12, 3, 128, [1000, 2, 515], [15, 16, 9], [1, 0, 1], 100, 16),
     (6, 2, 128, [700, 33], [9, 5], [0, 1], 0, 16),                 # Hq not a multiple of the combine's rows per wave
     (3, 3, 64, [400, 90], [7, 3], [1, 0], 0, 16),                  # Hq == Hkv == 3, head_dim 64
+    (16, 2, 264, [300, 41], [9, 10], [0, 1], 0, 16),               # 72 rows at padded head_dim 512: five row tiles
 ]
 
 
