@@ -48,8 +48,10 @@ typedef enum {
 } dflash_status;
 
 /* Merge of split-KV pieces (desc->merge_mode).  AUTO merges inside the attention kernel for
-   small grids (at most 64 workgroups: a launch-bound draft step, where a second kernel is a
-   large part of the call) and with the combine kernel otherwise (measured faster there). */
+   small steps -- head_dim <= 256 and at most 3 key tiles of work per compute unit (run on
+   at most one workgroup per CU), or a grid of at most 64 workgroups: launch-bound draft
+   steps, where a second kernel is a large part of the call -- and with the combine kernel
+   otherwise (measured faster there). */
 #define DFLASH_MERGE_AUTO 0
 #define DFLASH_MERGE_COMBINE_KERNEL 1
 #define DFLASH_MERGE_IN_KERNEL 2

@@ -100,10 +100,10 @@ int device_cus(int* out)
     return DFLASH_OK;
 }
 
-// Fewest key tiles per attention workgroup.  Small steps (a few requests of short
-// context) are latency-bound: a workgroup walks its tiles one after another, so
-// runs of one or two tiles (and a combine over more pieces) finish soonest;
-// large steps fill the chip long before this bound matters.
+// Fewest key tiles per attention workgroup for the reference kernel and for steps
+// above the small-step bound below: a workgroup walks its tiles one after another,
+// so short runs (and a combine over more pieces) finish soonest; large steps fill
+// the chip long before this bound matters.
 constexpr int kMinTilesPerWg = 2;
 // Set-up charge of a unit in the work split (decomp.h), in tiles: what one more
 // unit in a run costs the MFMA kernel (queries and first pages in, output or
@@ -117,11 +117,26 @@ constexpr int kSegmentCharge = 3;
 constexpr int kSegmentChargeShort = 2;
 constexpr int kChargeMinTiles = 16;
 constexpr size_t kAlign = 256;
-// Largest grid the automatic choice merges split units in: a small draft step is launch
+// Largest grid the automatic choice always merges split units in (besides the small steps
+// below, this matters for forced grids): a small draft step is launch
 // bound, and merging in the attention kernel saves the second launch (C1's step: 18.4 ->
 // 16.7 us per call); larger grids pay more for the in-kernel merge's coherent publish and
 // waits than for a second kernel (C2 48.7 vs 60.0 us, C3 138.7 vs 147.4 us; A/B on one box).
 constexpr int kMergeInKernelAutoWgs = 64;
+// A step at head_dim <= 256 whose work -- key tiles plus every unit's set-up charge --
+// comes to at most this many tiles per compute unit is latency-bound (a draft step: a
+// few requests, short contexts).  The automatic choice merges its split units inside the
+// attention kernel: with runs of one to three tiles a second launch costs more than the
+// coherent merge.  Where kMinTilesPerWg would give it more than kMergeInKernelAutoWgs
+// workgroups, it runs one per CU instead.  Measured per call (block append + attention,
+// GPU time, two boxes) against kMinTilesPerWg's grid and the combine kernel: head_dim 128
+// with 4 and 8 requests of 512 context keys 18.7-20.9 -> 17.7-20.0 and 18.9-21.5 ->
+// 16.3-19.0 us; head_dim 256, one request of 2.6K keys, 21.6-23.8 -> 21.0-23.3 us.  With
+// 1 or 2 requests kMinTilesPerWg gives at most 64 workgroups, which measured as fast as
+// one per CU or up to 0.5 us faster.  At head_dim 512 the in-kernel merge is slower even
+// for small steps (one request of 2048 keys: 33.7 -> 39.9 us), so those keep the
+// general rule.
+constexpr int kSmallStepTilesPerWg = 3;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -227,6 +242,7 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             occ = q;
     }
     int64_t P = (int64_t)cus * occ;
+    bool small_step = false;
     if (desc->total_kv_len > 0) {
         const int64_t B = desc->num_reqs;
         const int64_t keys = desc->total_kv_len;
@@ -235,6 +251,10 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             groups = ((int64_t)desc->max_block_len * G + p->rmax - 1) / p->rmax;
         const int64_t tiles = (int64_t)Hkv * groups * (keys / p->tk + B);
         P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles + kMinTilesPerWg - 1) / kMinTilesPerWg));
+        const int64_t work = tiles + (int64_t)Hkv * groups * B * kSegmentChargeShort;
+        small_step = kernel == DFLASH_KERNEL_MFMA && p->Dp <= 256 && work <= (int64_t)kSmallStepTilesPerWg * cus;
+        if (small_step && P > kMergeInKernelAutoWgs)
+            P = cus;
     }
     if (desc->num_workgroups > 0)
         P = desc->num_workgroups;
@@ -252,7 +272,7 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
         // [merge counters, a fixed layout for every grid (merge.h)]
         // [bf16 partials [P][2][rmax][Dp]] [fp32 log-sum-exps [P][2][rmax]]
         const bool want = desc->merge_mode == DFLASH_MERGE_IN_KERNEL ||
-                          (desc->merge_mode == DFLASH_MERGE_AUTO && p->P <= kMergeInKernelAutoWgs);
+                          (desc->merge_mode == DFLASH_MERGE_AUTO && (small_step || p->P <= kMergeInKernelAutoWgs));
         p->merge_in_kernel = kernel == DFLASH_KERNEL_MFMA && want && p->P <= dflash::kMergeMaxWgs;
         p->ctr_bytes = align_up((size_t)dflash::kCtrWords * sizeof(int32_t));
         const size_t o_bytes = (size_t)p->P * 2 * p->rmax * p->Dp * sizeof(uint16_t);

@@ -223,11 +223,41 @@ def test_plan_small_problem_uses_few_workgroups(lib):
     # 17 tiles per kv-head, two kv-heads: two tiles per workgroup, not the whole chip
     assert p.num_workgroups == 17
     assert p.head_dim_padded == 128 and p.rows_per_unit == 48
-    # a small grid merges its split units inside the attention kernel (one launch)
+    # a small step merges its split units inside the attention kernel (one launch)
     assert p.merge_in_kernel == 1 and p.combine_workgroups == 0
+    # four such requests: ceil(2 x (65 + 4) / 2) = 69 > 64 workgroups, but 154 flat positions
+    # (set-up charges of 2 included) are under 3 per CU: one workgroup per CU, merged in the kernel
+    p4 = nb.dflash_block_attn_plan(desc(num_reqs=4, total_q=36, total_kv_len=4 * 521, max_pages_per_req=33,
+                                        num_pages=136), 8, 2, 128)
+    assert p4.num_workgroups == 256 and p4.merge_in_kernel == 1 and p4.combine_workgroups == 0
     p2 = nb.dflash_block_attn_plan(desc(num_reqs=1, total_q=9, total_kv_len=521, max_pages_per_req=33, num_pages=34,
                                         merge_mode=nb.DFLASH_MERGE_COMBINE_KERNEL), 8, 2, 128)
     assert p2.merge_in_kernel == 0 and p2.combine_workgroups > 0
+
+
+def test_plan_small_step_bound(lib):
+    # head_dim 256, one request of block 9, Hq 32 / Hkv 8: 36 rows, one row group.  Work =
+    # 8 kv-heads x (keys // 32 + 1 tiles + a set-up charge of 2) = 8 * (keys // 32) + 24,
+    # which is 768 = 3 per CU at 3007 keys and 776 at 3008; two tiles per workgroup would
+    # take 376 > 64 workgroups, so the small step runs one per CU
+    def plan(keys):
+        return nb.dflash_block_attn_plan(desc(num_reqs=1, total_q=9, total_kv_len=keys, max_pages_per_req=256,
+                                              num_pages=256), 32, 8, 256)
+    small, large = plan(3007), plan(3008)
+    assert small.num_workgroups == 256 and small.merge_in_kernel == 1 and small.combine_workgroups == 0
+    assert large.merge_in_kernel == 0 and large.combine_workgroups > 0
+    # a forced small grid still merges in the kernel; a forced merge mode wins over both rules
+    forced = nb.dflash_block_attn_plan(desc(num_reqs=1, total_q=9, total_kv_len=3008, max_pages_per_req=256,
+                                            num_pages=256, num_workgroups=64), 32, 8, 256)
+    assert forced.num_workgroups == 64 and forced.merge_in_kernel == 1
+    sep = nb.dflash_block_attn_plan(desc(num_reqs=1, total_q=9, total_kv_len=3007, max_pages_per_req=256,
+                                         num_pages=256, merge_mode=nb.DFLASH_MERGE_COMBINE_KERNEL), 32, 8, 256)
+    assert sep.num_workgroups == 256 and sep.merge_in_kernel == 0 and sep.combine_workgroups > 0
+    # head_dim 512 keeps the general rule: ceil(4 kv-heads x (64 + 1) tiles / 2) workgroups,
+    # merged by the combine kernel
+    g = nb.dflash_block_attn_plan(desc(num_reqs=1, total_q=9, total_kv_len=2057, max_pages_per_req=256,
+                                       num_pages=256), 32, 4, 512)
+    assert g.num_workgroups == 130 and g.merge_in_kernel == 0 and g.combine_workgroups > 0
 
 
 def test_plan_reference_kernel_and_forced_grid(lib):
