@@ -179,6 +179,57 @@ def summarize_trace(csv_path: str) -> dict:
     return {"trace": csv_path, "phases": out}
 
 
+def summarize_timeline(stamps, call_us, tile_bytes: int) -> dict:
+    """Per-workgroup timeline of the attention kernel from the timeline build's stamps.
+
+    stamps: [calls][P][8] of the 100 MHz wall clock (words 0-3: start, first tile
+    loop, last tile loop end, end of the last epilogue; word 4: key tiles), call_us:
+    the events around each of those calls.  Per call, medians over the workgroups
+    that have tiles; reported as medians over calls.  Logical workgroup k runs on
+    XCD k // (P / 8) when P is a multiple of 8 (the kernel's XCD-major order)."""
+    import numpy as np
+
+    S = np.asarray(stamps, dtype=np.float64)
+    calls, P, _ = S.shape
+    keys = ["setup_us", "loop_us", "per_tile_us", "per_tile_p90_us", "epilogue_us", "last_after_median_us",
+            "span_us", "events_minus_span_us", "tiles_median", "tiles_max"]
+    rows = {k: [] for k in keys}
+    per_xcd = []
+    for c in range(calls):
+        s = S[c]
+        t0 = s[s[:, 0] > 0, 0].min()
+        rel = (s[:, :4] - t0) / 100.0
+        tiles = s[:, 4]
+        act = tiles > 0
+        setup = rel[act, 1] - rel[act, 0]
+        loop = rel[act, 2] - rel[act, 1]
+        per_tile = loop / tiles[act]
+        end = rel[s[:, 0] > 0, 3]
+        rows["setup_us"].append(np.median(setup))
+        rows["loop_us"].append(np.median(loop))
+        rows["per_tile_us"].append(np.median(per_tile))
+        rows["per_tile_p90_us"].append(np.percentile(per_tile, 90))
+        rows["epilogue_us"].append(np.median(rel[act, 3] - rel[act, 2]))
+        rows["last_after_median_us"].append(end.max() - np.median(end))
+        rows["span_us"].append(end.max())
+        rows["events_minus_span_us"].append(call_us[c] - end.max())
+        rows["tiles_median"].append(np.median(tiles[act]))
+        rows["tiles_max"].append(tiles.max())
+        if P % 8 == 0:
+            pt = np.full(P, np.nan)
+            pt[act] = per_tile
+            per = P // 8
+            per_xcd.append([np.nanmedian(pt[x * per:(x + 1) * per]) for x in range(8)])
+    out = {k: float(np.median(v)) for k, v in rows.items()}
+    out["calls"] = calls
+    out["workgroups"] = P
+    out["call_us"] = float(np.median(call_us))
+    out["loop_rate_gbps"] = P * tile_bytes / (out["per_tile_us"] * 1e-6) / 1e9
+    if per_xcd:
+        out["per_xcd_per_tile_us"] = [float(v) for v in np.median(np.asarray(per_xcd), axis=0)]
+    return out
+
+
 def gpu_info() -> dict:
     """Device name and CU count (no clocks: reading them would need a helper process,
     which must not be started from a process that has initialised the GPU)."""
@@ -504,6 +555,8 @@ def main(argv=None) -> int:
     ap.add_argument("--conv", action="store_true")
     ap.add_argument("--spans", action="store_true",
                     help="call dflash_block_attn_spans with seeded bidirectional spans (causal requests)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup timeline of the attention kernel (the timeline build of the library)")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
@@ -532,10 +585,18 @@ def main(argv=None) -> int:
 
         oracle.build()
 
+    import non_causal_block_amd as nb
+
+    if args.timeline:
+        # the library built with stamps; built (if missing) before this process touches the GPU
+        if not os.path.exists(nb._lib.TIMELINE_LIB_PATH):
+            from non_causal_block_amd import build as hipbuild
+            hipbuild.build(timeline=True)
+        nb._lib.LIB_PATH = nb._lib.TIMELINE_LIB_PATH
+
     import numpy as np
     import torch
 
-    import non_causal_block_amd as nb
     import workloads
 
     if args.graph_latency or args.conv:
@@ -586,6 +647,13 @@ def main(argv=None) -> int:
     flush.fill_(1.0)  # also the known-size write the WRITE_SIZE counter is calibrated with
     sink = torch.zeros(1, dtype=torch.int32, device=dev)  # receives the XOR of each pass
     stream = torch.cuda.current_stream(dev)
+
+    tl_buf, tl_snaps = None, []
+    if args.timeline:
+        tl_buf = torch.zeros(plan.num_workgroups * 8, dtype=torch.int64, device=dev)
+        st = nb.dflash_timeline_set_buffer(tl_buf, tl_buf.numel() * 8)
+        if st != nb.DFLASH_OK:
+            raise nb.DFlashError(st, nb.dflash_last_error_message())
 
     def stream_read():
         st = nb.dflash_stream_read(flush, FLUSH_BYTES, sink, stream.cuda_stream)
@@ -639,6 +707,8 @@ def main(argv=None) -> int:
     t_wall0 = time.perf_counter()
     for i in range(args.warmup, n_ev):
         step(i, False)
+        if tl_buf is not None:
+            tl_snaps.append(tl_buf.clone())  # this call's stamps, before the next call's
         step(i, True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -665,6 +735,14 @@ def main(argv=None) -> int:
           f"p90 {np.percentile(call_ms,90)*1e3:.1f}); attention kernel mean {att_ms.mean()*1e3:.1f} us; "
           f"K/V {kv_bytes/1e6:.1f} MB -> {achieved:.0f} GB/s kernel, {call_gbps:.0f} GB/s call; "
           f"wall {t_wall:.3f} s; streaming read {stream_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+
+    if tl_buf is not None:
+        stamps = torch.stack(tl_snaps).view(len(tl_snaps), plan.num_workgroups, 8).cpu().numpy()
+        tl = summarize_timeline(stamps, call_ms * 1e3, tile_bytes=plan.tile_keys * wl.D * 2 * 2)
+        print(json.dumps({"workload": args.config, "build": "timeline (libdflash_attn_timeline.so)",
+                          "kernel_sha": kernel_source_hash(), "attention_kernel_us": float(att_ms.mean() * 1e3),
+                          "timeline": tl, "gpu": gpu_info()}), flush=True)
+        return 0
 
     khash = kernel_source_hash()
     traffic = traffic_for(khash, kv_bytes)

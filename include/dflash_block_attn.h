@@ -325,6 +325,21 @@ int dflash_block_conv(const void* x, const void* base, const void* delta, const 
  */
 int dflash_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+#ifdef DFLASH_TIMELINE
+/*
+ * dflash_timeline_set_buffer -- exported only by the timeline build of the library
+ * (libdflash_attn_timeline.so, compiled with -DDFLASH_TIMELINE; the product library
+ * does not have it).  A measurement aid: every later MFMA attention launch whose grid
+ * of P workgroups fits in `bytes` (P * 64) writes, per logical workgroup w, the 100 MHz
+ * wall clock (wall_clock64) at buf[8w + 0] its start, [8w + 1] its first tile loop's
+ * start, [8w + 2] its last tile loop's end, [8w + 3] the end of its last epilogue
+ * (before any in-kernel merge), and [8w + 4] its key-tile count.  Workgroups without
+ * tiles leave [1] and [2] zero.  buf: device memory, caller-owned, 8-byte aligned;
+ * NULL with bytes = 0 turns the stamps off.  DFLASH_ERR_INVALID_ARGUMENT otherwise.
+ */
+int dflash_timeline_set_buffer(void* buf, size_t bytes);
+#endif
+
 #ifdef __cplusplus
 }
 #endif

@@ -100,6 +100,15 @@ def dflash_stream_read(buf, nbytes: int, sink, stream) -> int:
     return _lib.load().dflash_stream_read(_ptr(buf), nbytes, _ptr(sink), stream)
 
 
+def dflash_timeline_set_buffer(buf, nbytes: int) -> int:
+    """Timeline build only: per-workgroup stamps of later attention launches go to buf
+    (see the C header).  Raises if the loaded library is not the timeline build."""
+    lib = _lib.load()
+    if not hasattr(lib, "dflash_timeline_set_buffer"):
+        raise RuntimeError(f"{_lib.LIB_PATH} is not the timeline build (python -m non_causal_block_amd.build --timeline)")
+    return lib.dflash_timeline_set_buffer(_ptr(buf), nbytes)
+
+
 def dflash_status_string(status: int) -> str:
     return _lib.load().dflash_status_string(status).decode()
 

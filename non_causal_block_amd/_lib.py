@@ -11,6 +11,8 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdflash_attn.so")
+# the same library built with per-workgroup timeline stamps (a measurement aid)
+TIMELINE_LIB_PATH = os.path.join(_HERE, "libdflash_attn_timeline.so")
 
 DFLASH_OK = 0
 DFLASH_ERR_INVALID_ARGUMENT = 1
@@ -112,5 +114,8 @@ def load() -> ctypes.CDLL:
     lib.dflash_set_debug_checks.restype = ctypes.c_int
     lib.dflash_debug_checks_result.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32)]
     lib.dflash_debug_checks_result.restype = ctypes.c_int
+    if hasattr(lib, "dflash_timeline_set_buffer"):  # the timeline build only
+        lib.dflash_timeline_set_buffer.argtypes = [P, ctypes.c_size_t]
+        lib.dflash_timeline_set_buffer.restype = ctypes.c_int
     _lib = lib
     return lib

@@ -1,9 +1,12 @@
 """Build libdflash_attn.so (gfx950) in-tree with hipcc.
 
-    python -m non_causal_block_amd.build [--verbose]
+    python -m non_causal_block_amd.build [--verbose] [--timeline]
 
 Each csrc/*.hip is compiled to an object under _build/ (in parallel), then
-linked into non_causal_block_amd/libdflash_attn.so.  Every HIP compile line
+linked into non_causal_block_amd/libdflash_attn.so.  --timeline builds the same
+sources with -DDFLASH_TIMELINE (objects under _build/timeline/) into
+libdflash_attn_timeline.so, whose attention kernel also writes per-workgroup
+wall-clock stamps (dflash_timeline_set_buffer; `bench.py --timeline`).  Every HIP compile line
 turns off the packed-fp32 target feature (``-packed-fp32-ops``): ordinary
 float code must not be lowered to v_pk_* fp32 instructions on this target.
 """
@@ -23,6 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdflash_attn.so")
+TIMELINE_LIB = os.path.join(PKG, "libdflash_attn_timeline.so")
 ARCH = "gfx950"
 
 
@@ -40,9 +44,9 @@ COMMON = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, outdir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(outdir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,27 +60,31 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    outdir = os.path.join(BUILD, "timeline") if timeline else BUILD
+    lib = TIMELINE_LIB if timeline else LIB
+    defines = ("DFLASH_TIMELINE",) if timeline else ()
+    os.makedirs(outdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, outdir, defines), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--timeline", action="store_true", help="the timeline build (libdflash_attn_timeline.so)")
     args = ap.parse_args(argv)
-    print(build(verbose=args.verbose))
+    print(build(verbose=args.verbose, timeline=args.timeline))
     return 0
 
 

@@ -140,6 +140,20 @@ constexpr int kSmallStepTilesPerWg = 3;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+#ifdef DFLASH_TIMELINE
+// Timeline build: the caller's stamp buffer (dflash_timeline_set_buffer), used by the
+// MFMA attention kernel of every later call whose grid it holds (8 words per workgroup).
+std::mutex g_timeline_mu;
+uint64_t* g_timeline = nullptr;
+size_t g_timeline_bytes = 0;
+
+uint64_t* timeline_buffer(int64_t P)
+{
+    std::lock_guard<std::mutex> lk(g_timeline_mu);
+    return g_timeline && g_timeline_bytes >= (size_t)P * 8 * sizeof(uint64_t) ? g_timeline : nullptr;
+}
+#endif
+
 struct Plan {
     int kernel = 0;
     int P = 0;
@@ -410,6 +424,9 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     if (st != DFLASH_OK)
         return st;
     a.dbg = dbg;
+#ifdef DFLASH_TIMELINE
+    a.timeline = timeline_buffer(p.P);
+#endif
     if (dbg)
         call->check = validate_args(page_table, ctx_lens, block_lens, span_offsets, num_spans, window, p.tk, false,
                                     desc, dbg);
@@ -520,6 +537,18 @@ int set_last_error(int status, const char* msg)
 extern "C" {
 
 int dflash_abi_version(void) { return DFLASH_ABI_VERSION; }
+
+#ifdef DFLASH_TIMELINE
+int dflash_timeline_set_buffer(void* buf, size_t bytes)
+{
+    if ((buf == nullptr) != (bytes == 0) || reinterpret_cast<uintptr_t>(buf) % 8)
+        return fail(DFLASH_ERR_INVALID_ARGUMENT, "timeline buffer: NULL with 0 bytes, or 8-byte aligned with > 0");
+    std::lock_guard<std::mutex> lk(g_timeline_mu);
+    g_timeline = static_cast<uint64_t*>(buf);
+    g_timeline_bytes = bytes;
+    return DFLASH_OK;
+}
+#endif
 
 int dflash_block_conv(const void* x, const void* base, const void* delta, const int32_t* block_lens,
                        int32_t num_reqs, int32_t total_q, int32_t channels, int32_t groups, int32_t taps, void* out,

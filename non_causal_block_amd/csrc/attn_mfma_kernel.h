@@ -208,6 +208,14 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
 
     if (a.dbg && *a.dbg != 0u)
         return;  // debug checks found a bad device-side value: touch nothing
+#ifdef DFLASH_TIMELINE
+    // Timeline build: the 100 MHz wall clock when the workgroup starts, when its first
+    // tile loop starts and when its last one ends; its tile count.  Written with the
+    // end of its last epilogue (before any in-kernel merge) to
+    // timeline[8 * logical workgroup + {0, 1, 2, 3, 4}].
+    const uint64_t tl_start = wall_clock64();
+    uint64_t tl_loop0 = 0, tl_loop1 = 0, tl_tiles = 0;
+#endif
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     f32x4_t* sx = reinterpret_cast<f32x4_t*>(lds + C::OFF_SX);
     u32x4_t* px = reinterpret_cast<u32x4_t*>(lds + C::OFF_PX);
@@ -718,6 +726,11 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 return aborted;
             };
 
+#ifdef DFLASH_TIMELINE
+            if (tl_loop0 == 0)
+                tl_loop0 = wall_clock64();
+            tl_tiles += t1 - t0;
+#endif
             if constexpr (PHASE == 0) {
                 if (run_pass(std::integral_constant<int, kLazy>{})) {
                     if (this_seg < 64)
@@ -731,6 +744,9 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 run_pass(std::integral_constant<int, kFixed>{});
             }
 
+#ifdef DFLASH_TIMELINE
+            tl_loop1 = wall_clock64();
+#endif
             // ---------------- epilogue ----------------
 #pragma unroll
             for (int ob = 0; ob < NOWN; ++ob) {
@@ -859,6 +875,16 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     walk(std::integral_constant<int, 0>{});
     if (redo_mask != 0 || redo_overflow)
         walk(std::integral_constant<int, 1>{});
+#ifdef DFLASH_TIMELINE
+    if (threadIdx.x == 0 && a.timeline) {
+        uint64_t* tp = a.timeline + (int64_t)logical_wg(blockIdx.x, d.P) * 8;
+        tp[0] = tl_start;
+        tp[1] = tl_loop0;
+        tp[2] = tl_loop1;
+        tp[3] = wall_clock64();
+        tp[4] = tl_tiles;
+    }
+#endif
     if (!a.ctr)
         return;  // the combine kernel merges the partials
 

@@ -282,6 +282,11 @@ struct AttnArgs {
     int32_t max_pages_per_req;
     float scale_log2;  // scale * log2(e)
     const uint32_t* dbg;  // debug-check state or nullptr: when it is non-zero the kernel does nothing
+#ifdef DFLASH_TIMELINE
+    // Timeline build only: per-workgroup wall-clock stamps (layout in attn_mfma_kernel.h),
+    // or nullptr for none.
+    uint64_t* timeline;
+#endif
 };
 
 struct CombineArgs {

@@ -24,10 +24,17 @@ def lib():
     return _lib.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+TIMELINE_BLOCK = r"#ifdef DFLASH_TIMELINE(.*?)#endif"
+
+
+def _functions(text):
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dflash_\w+)\s*\(", text, flags=re.M)))
+
+
+def declared_functions():
+    """Functions the product library exports (the timeline build's extra one aside)."""
+    return _functions(re.sub(TIMELINE_BLOCK, "", open(HEADER).read(), flags=re.S))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -35,6 +42,12 @@ def test_every_declared_symbol_is_exported(lib):
     assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_timeline_setter_is_only_in_the_timeline_build(lib):
+    blocks = re.findall(TIMELINE_BLOCK, open(HEADER).read(), flags=re.S)
+    assert [_functions(b) for b in blocks] == [["dflash_timeline_set_buffer"]]
+    assert not hasattr(lib, "dflash_timeline_set_buffer")
 
 
 def test_stream_read_rejects_bad_arguments(lib):

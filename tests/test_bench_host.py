@@ -67,6 +67,35 @@ def test_counter_means_per_kernel(tmp_path):
     assert means["other"] == pytest.approx(5.0)
 
 
+def test_timeline_summary_of_synthetic_stamps():
+    import numpy as np
+
+    # two calls, 16 workgroups (2 per XCD); stamps in 100 MHz ticks.  Workgroup w starts at
+    # 10 + w ticks, spends 300 ticks (3 us) setting up, then tiles of 100 + 10 * (w // 2)
+    # ticks (1 us, +0.1 us per XCD), 40 of them, then 400 ticks (4 us) of epilogue
+    P, calls = 16, 2
+    S = np.zeros((calls, P, 8), dtype=np.int64)
+    for c in range(calls):
+        for w in range(P):
+            tile = 100 + 10 * (w // 2)
+            S[c, w, 0] = 10 + w
+            S[c, w, 1] = S[c, w, 0] + 300
+            S[c, w, 2] = S[c, w, 1] + 40 * tile
+            S[c, w, 3] = S[c, w, 2] + 400
+            S[c, w, 4] = 40
+    out = bench.summarize_timeline(S, np.array([100.0, 110.0]), tile_bytes=65536)
+    assert out["setup_us"] == pytest.approx(3.0)
+    assert out["epilogue_us"] == pytest.approx(4.0)
+    assert out["per_xcd_per_tile_us"] == pytest.approx([1.0 + 0.1 * x for x in range(8)])
+    assert out["per_tile_us"] == pytest.approx(1.35)  # median of the 16 workgroups' 1.0 .. 1.7
+    ends = [(10 + w + 300 + 40 * (100 + 10 * (w // 2)) + 400 - 10) / 100 for w in range(P)]
+    assert out["span_us"] == pytest.approx(max(ends))
+    assert out["last_after_median_us"] == pytest.approx(max(ends) - np.median(ends))
+    assert out["events_minus_span_us"] == pytest.approx(105.0 - max(ends))
+    assert out["tiles_median"] == 40 and out["calls"] == 2
+    assert out["loop_rate_gbps"] == pytest.approx(16 * 65536 / 1.35e-6 / 1e9)
+
+
 def test_cpu_model_is_named():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
 
