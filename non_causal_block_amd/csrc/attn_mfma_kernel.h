@@ -395,6 +395,11 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
             __builtin_amdgcn_sched_barrier(0);
 
             // ---------------- Q^T (B operand) for the unit ----------------
+            // All of the unit's Q chunks are requested here; padding rows and absent d-chunks
+            // (which read a real row) are zeroed only after the first tile's K/V requests
+            // (q_mask below), so that nothing waits for Q before those go out.  Zeroing each
+            // row tile as it arrived made the compiler wait for every row tile's loads in
+            // turn (five dependent rounds at head_dim 512) before the first K/V request.
             bf16x8_t qf[RT][KS];
 #pragma unroll
             for (int b = 0; b < RT; ++b) {
@@ -405,16 +410,25 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 const int32_t qj = rr % G;
                 const uint16_t* qrow = a.q + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    u32x4_t x = ldg16(qrow + (dval[s] ? wbase + 32 * s + 8 * grp4 : 0));
-                    const bool keep = rv && dval[s];
-                    x[0] = keep ? x[0] : 0u;
-                    x[1] = keep ? x[1] : 0u;
-                    x[2] = keep ? x[2] : 0u;
-                    x[3] = keep ? x[3] : 0u;
-                    qf[b][s] = as_bf16x8(x);
-                }
+                for (int s = 0; s < KS; ++s)
+                    qf[b][s] = as_bf16x8(ldg16(qrow + (dval[s] ? wbase + 32 * s + 8 * grp4 : 0)));
             }
+            auto q_mask = [&]() {
+#pragma unroll
+                for (int b = 0; b < RT; ++b) {
+                    const bool rv = b * 16 + l16 < rows_here;
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        u32x4_t x = __builtin_bit_cast(u32x4_t, qf[b][s]);
+                        const bool keep = rv && dval[s];
+                        x[0] = keep ? x[0] : 0u;
+                        x[1] = keep ? x[1] : 0u;
+                        x[2] = keep ? x[2] : 0u;
+                        x[3] = keep ? x[3] : 0u;
+                        qf[b][s] = as_bf16x8(x);
+                    }
+                }
+            };
 
 
             float m_fix[NOWN];
@@ -507,6 +521,8 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (MODE != kMaxScan)
                     issue_v(vr);
+                __builtin_amdgcn_sched_barrier(0);
+                q_mask();  // idempotent: a second pass over the segment zeroes the same lanes
                 __builtin_amdgcn_sched_barrier(0);
                 // One tile; PF: also request the next one (every tile but the segment's last).
                 auto step = [&](const int32_t t, auto pf_tag) {
