@@ -170,6 +170,8 @@ struct Plan {
     size_t ctr_bytes = 0;  // merge counters at the start of the workspace
     size_t off_o = 0;
     size_t off_lse = 0;
+    size_t off_dir = 0;  // merge directory (MFMA kernel), 0 = none
+    bool use_dir = false;  // the attention kernel writes it for the rows-per-wave combine
     size_t ws_bytes = 0;
     bool empty = false;
 };
@@ -293,6 +295,13 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
         p->off_o = p->ctr_bytes;
         p->off_lse = p->off_o + align_up(o_bytes);
         p->ws_bytes = p->off_lse + align_up((size_t)p->P * 2 * p->rmax * sizeof(float));
+        if (kernel == DFLASH_KERNEL_MFMA) {
+            // [merge directory: one 8-byte entry per output row, written by the attention
+            // kernel for the combine kernel; present whatever the merge mode, so the
+            // workspace size does not depend on it]
+            p->off_dir = p->ws_bytes;
+            p->ws_bytes = p->off_dir + align_up((size_t)desc->total_q * Hq * 8);
+        }
         if (p->merge_in_kernel)
             return DFLASH_OK;
         p->combine_lpr = kernel == DFLASH_KERNEL_MFMA ? dflash::combine_lanes_per_row(p->Dp, Hq) : 64;
@@ -312,6 +321,12 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             p->combine_rows = true;
             p->combine_wgs = (int)rows;
         }
+        // Up to head_dim 256 the rows-per-wave combine finds each row's pieces in the merge
+        // directory: one load instead of a pass over the request arrays, a reload of the
+        // row's lengths and the work-split arithmetic (calls: C4 43.8 -> 42.2 us, C2 46.9 ->
+        // 46.3 us, A/B on one box).  At head_dim 512 (and in the workgroup-per-row combine,
+        // bound by its partial reads) it measured no faster, so those keep the request arrays.
+        p->use_dir = p->off_dir != 0 && !p->combine_rows && p->Dp <= 256;
     }
     return DFLASH_OK;
 }
@@ -402,6 +417,8 @@ int attn_prepare(const void* q, const void* k_pages, const void* v_pages, const 
     a.part_o = p.ws_bytes ? reinterpret_cast<uint16_t*>(ws + p.off_o) : nullptr;
     a.part_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
     a.ctr = p.merge_in_kernel ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+    a.dir = p.use_dir ? reinterpret_cast<uint2*>(ws + p.off_dir) : nullptr;
+    a.total_rows = (int64_t)desc->total_q * n_heads;
     a.k_new = a.v_new = nullptr;  // set by dflash_block_attn_append for the fused launch
     a.k_dst = a.v_dst = nullptr;
     a.app_dk = a.app_dv = 0;
@@ -458,6 +475,7 @@ int attn_launch(const AttnCall& call, const dflash_batch_desc* desc, hipStream_t
         c.block_lens = a.block_lens;
         c.part_o = a.part_o;
         c.part_lse = a.part_lse;
+        c.dir = a.dir;
         c.out = a.out;
         c.d = a.d;
         c.Hq = a.Hq;

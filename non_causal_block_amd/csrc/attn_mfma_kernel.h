@@ -205,6 +205,10 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     // Otherwise V of the next tile is requested after this wave's S^T products, or, where a
     // wave owns two row tiles, after the first barrier.
     constexpr bool V_AFTER_BARRIER = !LATE_V && RT > WAVES;
+    // Instances that write the merge directory (AttnArgs::dir; the planner passes one only
+    // up to head_dim 256): at head_dim 512 the directory measured no faster in the combine,
+    // and its epilogue checks alone cost the attention kernel about 1% on C3.
+    constexpr bool DIR = DP <= 256;
 
     if (a.dbg && *a.dbg != 0u)
         return;  // debug checks found a bad device-side value: touch nothing
@@ -255,9 +259,14 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     for (int s = 0; s < KS; ++s)
         dval[s] = EXACT || (wbase + 32 * s + 8 * grp4 < D);
 
-    int64_t total, begin, end;
+    int64_t total, begin, end, qtotal;
     RunStart first;
-    wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first);
+    wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first, qtotal);
+    if (DIR && total == 0 && a.dir && wg == 0) {
+        // no request has queries: every row of the merge directory is no request's
+        for (int64_t R = threadIdx.x; R < a.total_rows; R += C::THREADS)
+            a.dir[R] = make_uint2(0u, 0u);
+    }
     if (begin >= end)
         return;
     // The split units this run holds a piece of (slot 0: its first unit, slot 1: its
@@ -268,9 +277,17 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     // before this piece's arrival; [7] of slot 0 is the run length per workgroup.
     int64_t* rec_s = reinterpret_cast<int64_t*>(lds + C::OFF_REC);
     int have_rec = 0;
-    if (a.ctr && threadIdx.x == 0)
+    // What the epilogues and the end of the run need, kept in LDS rather than in registers
+    // through the tile loop: [7] the run length per workgroup, [12] the query tokens of
+    // all requests if this run holds the last tile (else -1), [13] the merge directory's
+    // rows, [14] its address (0: none).
+    if (threadIdx.x == 0 && (DIR || a.ctr))
         rec_s[7] = tiles_per_wg(total, d.P);
-
+    if (DIR && threadIdx.x == 0) {
+        rec_s[12] = qtotal;
+        rec_s[13] = a.total_rows;
+        rec_s[14] = reinterpret_cast<int64_t>(a.dir);
+    }
     // Segments of this workgroup's run that a lazy pass abandoned (bit i: i-th segment;
     // segments past 63 share the overflow flag and are all recomputed).
     uint64_t redo_mask = 0;
@@ -821,6 +838,28 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                             __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(dst));
                     }
                 }
+                // Merge directory (AttnArgs::dir): the unit's second piece writes its rows'
+                // entries.  That run began inside the unit, less than one run length past its
+                // first real tile, so the first piece is the previous workgroup.  It is a run
+                // inside the unit unless the unit has two pieces, so the work stays off the
+                // runs that cross into a second unit, which end last.
+                if (DIR && slot == 0 && t0 > 0) {
+                    uint2* const dirp = reinterpret_cast<uint2*>(rec_s[14]);
+                    const int64_t tpw = rec_s[7];
+                    if (dirp && t0 <= tpw) {
+                        const int64_t us = rbase + (int64_t)unit * g.uwork;
+                        const int64_t kf = wg - 1;
+                        const int64_t kl = (us + g.uwork - 1) / tpw;
+                        const uint2 e = dir_pack(kf, kf * tpw < us ? 1 : 0, kl - kf + 1, 0);
+                        const int64_t nrows = rec_s[13];
+                        for (int row = threadIdx.x; row < rows_here; row += C::THREADS) {
+                            const int32_t rr = row0 + row;
+                            const int64_t R = (qstart + rr / G) * a.Hq + (int64_t)kvh * G + rr % G;
+                            if (R < nrows)  // (total_q below the blocks' sum breaks the contract)
+                                dirp[R] = make_uint2(e.x, e.y | ((uint32_t)row << 24));
+                        }
+                    }
+                }
                 if (wave == 0 && grp4 == 0) {
 #pragma unroll
                     for (int b = 0; b < RT; ++b) {
@@ -843,8 +882,13 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
                         const int32_t rr = row0 + row;
                         const int32_t qi = rr / G;
                         const int32_t qj = rr % G;
-                        uint16_t* orow = a.out + ((qstart + qi) * a.Hq + (int64_t)kvh * G + qj) * D;
-                        *reinterpret_cast<u32x4_t*>(orow + ch * 8) = x;
+                        const int64_t R = (qstart + qi) * a.Hq + (int64_t)kvh * G + qj;
+                        *reinterpret_cast<u32x4_t*>(a.out + R * D + ch * 8) = x;
+                        if constexpr (DIR) {
+                            uint2* const dirp = reinterpret_cast<uint2*>(rec_s[14]);
+                            if (ch == 0 && dirp && R < rec_s[13])
+                                dirp[R] = make_uint2(0u, 1u);  // merge directory: nothing to merge
+                        }
                     }
                 }
             }
@@ -889,6 +933,13 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     };
 
     walk(std::integral_constant<int, 0>{});
+    if (DIR && rec_s[14] != 0 && rec_s[12] >= 0) {
+        // the run holding the last tile: rows of tokens past the last request's block
+        // (total_q larger than the blocks' sum) belong to no request
+        uint2* const dirp = reinterpret_cast<uint2*>(rec_s[14]);
+        for (int64_t R = rec_s[12] * a.Hq + threadIdx.x; R < rec_s[13]; R += C::THREADS)
+            dirp[R] = make_uint2(0u, 0u);
+    }
     if (redo_mask != 0 || redo_overflow)
         walk(std::integral_constant<int, 1>{});
 #ifdef DFLASH_TIMELINE

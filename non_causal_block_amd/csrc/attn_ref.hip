@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kRefThreads) void attn_ref_kernel(AttnArgs a)
 
     int64_t total, begin, end;
     RunStart first;
-    wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first);
+    int64_t qtotal;
+    wave_locate_run(a.ctx_lens, a.block_lens, a.causal, d, wg, total, begin, end, first, qtotal);
     if (begin >= end)
         return;
     int32_t r = first.r;

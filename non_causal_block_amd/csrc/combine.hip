@@ -44,32 +44,46 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
     const int64_t t = row0 / a.Hq;
     const int32_t h = (int32_t)(row0 % a.Hq) + rg;
 
-    int32_t r;
-    int64_t qstart, rbase, total;
-    wave_locate_token(a.ctx_lens, a.block_lens, d, t, r, qstart, rbase, total);
-    if (r >= d.B)
-        return;  // token past the real total
-    const int32_t L = a.ctx_lens[r];
-    const int32_t n = a.block_lens[r];
-    const ReqGeom g = req_geom(L, n, d);
-    const int64_t tpw = tiles_per_wg(total, d.P);
+    int64_t kf, np, us, tpw;
+    int32_t rin;
+    if (a.dir) {
+        // the attention kernel's directory: pieces kf .. kf+np-1; piece_slot(k, kf + slot0, 1)
+        // then gives the first piece's slot and slot 0 for the later ones
+        const DirEntry e = dir_unpack(a.dir[row0 + rg]);
+        kf = e.kf;
+        np = e.kf + e.np <= d.P ? e.np : 0;  // (always within the grid for this call's entries)
+        us = kf + e.slot0;
+        tpw = 1;
+        rin = e.rin;
+    } else {
+        int32_t r;
+        int64_t qstart, rbase, total;
+        wave_locate_token(a.ctx_lens, a.block_lens, d, t, r, qstart, rbase, total);
+        if (r >= d.B)
+            return;  // token past the real total
+        const int32_t L = a.ctx_lens[r];
+        const int32_t n = a.block_lens[r];
+        const ReqGeom g = req_geom(L, n, d);
+        tpw = tiles_per_wg(total, d.P);
 
-    const int32_t i = (int32_t)(t - qstart);
-    const int32_t kvh = h / d.G;
-    const int32_t j = h % d.G;
-    const int32_t rowreq = i * d.G + j;
-    const int32_t grp = rowreq / d.rmax;
-    const int32_t rin = rowreq % d.rmax;
-    const int32_t unit = kvh * g.ngroups + grp;
-    const int64_t us = rbase + (int64_t)unit * g.uwork;
-    int64_t kf, kl;
-    unit_pieces(g, us, d.ov, tpw, kf, kl);
+        const int32_t i = (int32_t)(t - qstart);
+        const int32_t kvh = h / d.G;
+        const int32_t j = h % d.G;
+        const int32_t rowreq = i * d.G + j;
+        const int32_t grp = rowreq / d.rmax;
+        rin = rowreq % d.rmax;
+        const int32_t unit = kvh * g.ngroups + grp;
+        us = rbase + (int64_t)unit * g.uwork;
+        int64_t kl;
+        unit_pieces(g, us, d.ov, tpw, kf, kl);
+        np = kl - kf + 1;
+    }
     // a unit finished inside one workgroup is already written; its lanes only take
     // part in the wave's shuffles
-    const bool split = kf != kl;
+    const bool split = np > 1;
     if (!__any(split))
         return;
-    const int64_t npieces = split ? kl - kf + 1 : 0;
+    const int64_t npieces = split ? np : 0;
     // loop bounds common to the wave (one row per wave: already uniform)
     int64_t max_np = npieces;
     if constexpr (RPW > 1) {

@@ -149,11 +149,13 @@ struct RunStart {
 // request.  For up to 64 requests everything, the causal flags included, comes from
 // one load of the request arrays (one memory round trip before the first segment);
 // larger batches take the general helpers.  When begin >= end `rs` is not set.
-// Wave-uniform.
+// qtotal: the query tokens of all requests when the run holds the last tile (end ==
+// total) or there is no work at all, else -1.  Wave-uniform.
 __device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_lens,
                                                 const int32_t* __restrict__ block_lens,
                                                 const uint8_t* __restrict__ causal, const Decomp& d, int32_t wg,
-                                                int64_t& total, int64_t& begin, int64_t& end, RunStart& rs)
+                                                int64_t& total, int64_t& begin, int64_t& end, RunStart& rs,
+                                                int64_t& qtotal)
 {
     const int lane = threadIdx.x & 63;
     if (d.B <= 64) {
@@ -168,6 +170,7 @@ __device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_
         const int64_t tpw = tiles_per_wg(total, d.P);
         begin = (int64_t)wg * tpw;
         end = min(total, begin + tpw);
+        qtotal = (end == total || total == 0) ? shfl_i64(qincl, 63) : -1;
         if (begin >= end)
             return;
         const unsigned long long m = __ballot(wincl > begin);
@@ -184,6 +187,14 @@ __device__ __forceinline__ void wave_locate_run(const int32_t* __restrict__ ctx_
     const int64_t tpw = tiles_per_wg(total, d.P);
     begin = (int64_t)wg * tpw;
     end = min(total, begin + tpw);
+    qtotal = -1;
+    if (end == total || total == 0) {
+        qtotal = 0;
+        for (int32_t base = 0; base < d.B; base += 64) {
+            const int64_t nn = (base + lane < d.B) ? (int64_t)block_lens[base + lane] : 0;
+            qtotal += shfl_i64(wave_inclusive_scan(nn), 63);
+        }
+    }
     if (begin >= end)
         return;
     wave_find_request(ctx_lens, block_lens, d, begin, rs.r, rs.rbase);
@@ -282,12 +293,42 @@ struct AttnArgs {
     int32_t max_pages_per_req;
     float scale_log2;  // scale * log2(e)
     const uint32_t* dbg;  // debug-check state or nullptr: when it is non-zero the kernel does nothing
+    // Merge directory for the rows-per-wave combine kernel, one entry per output row
+    // (token * Hq + q-head) of [0, total_rows): written in full by every launch whose
+    // partials that kernel merges, nullptr otherwise.  Entry (x, y): x = first piece's workgroup kf | that
+    // piece's slot << 31; y = pieces np (bits 0-23) | the row's index inside its unit << 24.
+    // np = 1: the unit was finished whole (nothing to merge); np = 0: a row of no request.
+    uint2* dir;
+    int64_t total_rows;  // total_q hint * Hq (rows of `dir`)
 #ifdef DFLASH_TIMELINE
     // Timeline build only: per-workgroup wall-clock stamps (layout in attn_mfma_kernel.h),
     // or nullptr for none.
     uint64_t* timeline;
 #endif
 };
+
+// Merge-directory entries (AttnArgs::dir).
+__device__ __forceinline__ uint2 dir_pack(int64_t kf, int slot0, int64_t np, int32_t rin)
+{
+    return make_uint2((uint32_t)kf | ((uint32_t)slot0 << 31), (uint32_t)np | ((uint32_t)rin << 24));
+}
+
+struct DirEntry {
+    int64_t kf;   // first piece's workgroup
+    int64_t np;   // pieces (0: no request's row, 1: finished whole)
+    int slot0;    // slot of the first piece's partial (the later pieces use slot 0)
+    int32_t rin;  // row inside its unit
+};
+
+__device__ __forceinline__ DirEntry dir_unpack(uint2 e)
+{
+    DirEntry r;
+    r.kf = e.x & 0x7fffffffu;
+    r.slot0 = (int)(e.x >> 31);
+    r.np = e.y & 0xffffffu;
+    r.rin = (int32_t)(e.y >> 24);
+    return r;
+}
 
 struct CombineArgs {
     const int32_t* ctx_lens;
@@ -301,6 +342,9 @@ struct CombineArgs {
     int32_t Dp;
     int64_t total_rows;  // total_q hint * Hq
     const uint32_t* dbg;  // as in AttnArgs
+    // the attention kernel's merge directory (AttnArgs::dir), or nullptr: then each row's
+    // pieces are derived from the request arrays (combine_row_kernel always does that)
+    const uint2* dir;
 };
 
 struct ConvArgs {

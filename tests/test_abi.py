@@ -218,9 +218,10 @@ def test_plan_mfma_global_layer(lib):
     assert p.rows_per_unit == 80 and p.head_dim_padded == 512 and p.tile_keys == 32
     assert p.num_workgroups == 256  # planning without a device assumes one workgroup per CU
     # merge counters (arrivals, claims per workgroup, one finish count), then two slots per
-    # workgroup: bf16 partial rows and fp32 log-sum-exps
+    # workgroup: bf16 partial rows and fp32 log-sum-exps, then the merge directory (8 bytes
+    # per output row)
     P = p.num_workgroups
-    assert p.workspace_bytes >= (2 * P + 1) * 4 + P * 2 * 80 * 512 * 2 + P * 2 * 80 * 4
+    assert p.workspace_bytes >= (2 * P + 1) * 4 + P * 2 * 80 * 512 * 2 + P * 2 * 80 * 4 + 36 * 32 * 8
     # a grid of 256: the combine kernel merges (16 units over 256 runs, about 18 pieces each,
     # so one combine workgroup per output row)
     assert p.merge_in_kernel == 0 and p.combine_workgroups == 36 * 32

@@ -154,3 +154,47 @@ def test_grid_larger_than_the_chip(D):
     H.assert_parity(H.to_f64(out), ref, f"D={D} grid {nwg}")
     _within_one_ulp(H.to_f64(out), H.to_f64(sep), f"D={D} grid {nwg}")
     assert not _counters(ws).any()
+
+
+@pytest.mark.parametrize("nwg", [24, 200])
+def test_combine_directory_rows_of_no_request(nwg):
+    """The combine kernel finds each output row's pieces in a directory that the attention
+    kernel writes on every call (one entry per row of the total_q hint).  Rows past the
+    blocks' sum belong to no request: a call must leave them alone even when an earlier
+    call on the same workspace had real rows there, and a call whose blocks are all empty
+    must leave every row alone.  Head_dim 256 (the directory's instances); 24 workgroups
+    split each unit a few ways, 200 many."""
+    big = workloads.build(3, 8, 2, 256, [3000, 900, 2000], [9, 9, 9], [0, 1, 0], seed=51)
+    small = workloads.build(2, 8, 2, 256, [2500, 1200], [9, 4], [1, 0], seed=52)
+    empty = workloads.build(2, 8, 2, 256, [300, 100], [0, 0], [0, 0], seed=53)
+    extra = 5
+
+    def call(wl, t, ws, total_q, out):
+        d = nb.make_desc(num_reqs=wl.B, total_q=total_q, max_block_len=9, total_kv_len=wl.total_kv,
+                         page_size=wl.page_size, max_pages_per_req=wl.max_pages_per_req, num_pages=wl.num_pages,
+                         num_workgroups=nwg, merge_mode=nb.DFLASH_MERGE_COMBINE_KERNEL)
+        plan = nb.dflash_block_attn_plan(d, wl.Hq, wl.Hkv, wl.D)
+        assert plan.combine_workgroups > 0 and ws.numel() >= plan.workspace_bytes
+        d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
+        st = nb.dflash_block_attn(t["q"], t["k"], t["v"], t["pt"], t["ctx"], t["blk"], wl.Hq, wl.Hkv, wl.D,
+                                  t["causal"], wl.window, wl.scale, out, torch.cuda.current_stream().cuda_stream, d)
+        assert st == nb.DFLASH_OK, nb.dflash_last_error_message()
+        torch.cuda.synchronize()
+        return plan
+
+    tb, ts, te = H.upload(big), H.upload(small), H.upload(empty)
+    te["q"] = ts["q"]  # no row of it is read: every block is empty
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=H.dev())
+    out_b = torch.empty((big.total_q, big.Hq, big.D), dtype=torch.bfloat16, device=H.dev())
+    call(big, tb, ws, big.total_q, out_b)
+    H.assert_parity(H.to_f64(out_b), oracle.run_workload(big), f"big, grid {nwg}")
+
+    nq = small.total_q + extra
+    out_s = torch.full((nq, small.Hq, small.D), 7.0, dtype=torch.bfloat16, device=H.dev())
+    call(small, ts, ws, nq, out_s)
+    H.assert_parity(H.to_f64(out_s[:small.total_q]), oracle.run_workload(small), f"small, grid {nwg}")
+    assert torch.all(out_s[small.total_q:] == 7.0), "rows of no request were written"
+
+    out_e = torch.full((4, empty.Hq, empty.D), 7.0, dtype=torch.bfloat16, device=H.dev())
+    call(empty, te, ws, 4, out_e)
+    assert torch.all(out_e == 7.0), "a call with empty blocks wrote output rows"
