@@ -9,7 +9,11 @@
 //     combine kernel derives from the unit's own tile range,
 //   * no slot of a workgroup is written twice,
 //   * no two split units share their first workgroup (the in-kernel merge names a
-//     unit's counters by it) and that workgroup exists.
+//     unit's counters by it) and that workgroup exists,
+//   * exactly one workgroup of a split unit writes its merge-directory entries (the
+//     attention kernel's rule: the run's first segment began inside the unit's real
+//     tiles, at most one run length past its first one), and what it derives -- first
+//     piece = previous workgroup, last piece, first piece's slot -- is the unit's own.
 // Prints "OK <units> <split units> <max pieces>" or "FAIL <reason>".
 #include <cstdio>
 #include <cstdlib>
@@ -47,6 +51,8 @@ int main()
     // (request, unit, real tile) -> times processed
     std::map<std::tuple<int, int, int>, int> tile_hits;
     std::set<std::pair<int64_t, int>> slots_used;
+    // unit key -> directory entries written: (first piece, last piece, first piece's slot)
+    std::map<std::tuple<int, int, int>, std::vector<std::tuple<int64_t, int64_t, int>>> dir_writes;
     for (int64_t wg = 0; wg < d.P; ++wg) {
         const int64_t begin = wg * tpw;
         const int64_t end = std::min<int64_t>(total, begin + tpw);
@@ -90,6 +96,12 @@ int main()
                     printf("FAIL partial segment in the middle of a run\n");
                     return 1;
                 }
+                if (slot == 0 && sg.t0 > 0 && sg.t0 <= tpw) {  // the directory's writer
+                    const int64_t us = rb + (int64_t)sg.unit * g.uwork;
+                    const int64_t kf = wg - 1;
+                    const int64_t kl = (us + g.uwork - 1) / tpw;
+                    dir_writes[{r, kvh, grp}].push_back({kf, kl, kf * tpw < us ? 1 : 0});
+                }
             }
             ++seg;
         }
@@ -118,12 +130,22 @@ int main()
                 const int64_t us = rbase[r] + (int64_t)unit * g.uwork;
                 int64_t kf, kl;
                 unit_pieces(g, us, d.ov, tpw, kf, kl);
+                const auto& dw = dir_writes[{r, kvh, grp}];
                 if (kf == kl) {
                     if (pl.size() != 1 || !std::get<2>(pl[0])) {
                         printf("FAIL unit not whole in one workgroup\n");
                         return 1;
                     }
+                    if (!dw.empty()) {
+                        printf("FAIL directory entries written for a whole unit\n");
+                        return 1;
+                    }
                     continue;
+                }
+                if (dw.size() != 1 || std::get<0>(dw[0]) != kf || std::get<1>(dw[0]) != kl ||
+                    std::get<2>(dw[0]) != piece_slot(kf, us, tpw)) {
+                    printf("FAIL directory writer of a split unit (%zu writers)\n", dw.size());
+                    return 1;
                 }
                 ++split;
                 max_pieces = std::max(max_pieces, pl.size());
