@@ -268,12 +268,14 @@ def test_determinism_is_bitwise():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+@pytest.mark.parametrize("name,B", [("c5_mixed_d512", 12), ("c2_paged_d256", 8)])
 @pytest.mark.parametrize("mode", [nb.DFLASH_MERGE_COMBINE_KERNEL, nb.DFLASH_MERGE_IN_KERNEL])
-def test_poison_and_guard_bands(mode):
+def test_poison_and_guard_bands(mode, name, B):
     """NaN page tails and unused pages never reach the output; rows of `out` outside
     the call's range are never written, and nothing outside the call's workspace is
-    written (guard bands on both sides of it)."""
-    wl = workloads.make("c5_mixed_d512", ctx_cap=700, B=12)   # pages are NaN-poisoned
+    written (guard bands on both sides of it).  Head_dim 256 with the combine kernel
+    also covers the merge directory at the workspace's end."""
+    wl = workloads.make(name, ctx_cap=700, B=B)   # pages are NaN-poisoned
     ref = oracle.run_workload(wl)
     t = H.upload(wl)
     guard = 7
