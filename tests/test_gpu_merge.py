@@ -198,3 +198,38 @@ def test_combine_directory_rows_of_no_request(nwg):
     out_e = torch.full((4, empty.Hq, empty.D), 7.0, dtype=torch.bfloat16, device=H.dev())
     call(empty, te, ws, 4, out_e)
     assert torch.all(out_e == 7.0), "a call with empty blocks wrote output rows"
+
+
+def test_combine_directory_more_than_64_requests():
+    """As above with 130 requests, where each run is located over several 64-request chunks
+    of the length arrays and the run holding the last tile sums the blocks in a pass of
+    its own: an earlier call with more query tokens leaves real entries in the rows that
+    the later call's larger total_q hint covers but no request owns."""
+    rng = np.random.default_rng(91)
+    B = 130
+    L = rng.integers(0, 400, size=B)
+    c = rng.integers(0, 2, size=B)
+    n_big = rng.integers(1, 10, size=B)
+    n_small = np.minimum(n_big, rng.integers(0, 6, size=B))
+    big = workloads.build(B, 8, 2, 128, L, n_big, c, seed=92)
+    small = workloads.build(B, 8, 2, 128, L, n_small, c, seed=93)
+    assert small.total_q < big.total_q
+    ws = torch.zeros(32 << 20, dtype=torch.uint8, device=H.dev())
+    for nwg in (24, 200):
+        for wl, total_q in ((big, big.total_q), (small, big.total_q)):
+            t = H.upload(wl)
+            d = nb.make_desc(num_reqs=wl.B, total_q=total_q, max_block_len=int(wl.block_lens.max()),
+                             total_kv_len=wl.total_kv, page_size=wl.page_size,
+                             max_pages_per_req=wl.max_pages_per_req, num_pages=wl.num_pages,
+                             num_workgroups=nwg, merge_mode=nb.DFLASH_MERGE_COMBINE_KERNEL)
+            plan = nb.dflash_block_attn_plan(d, wl.Hq, wl.Hkv, wl.D)
+            assert plan.combine_workgroups > 0 and ws.numel() >= plan.workspace_bytes
+            d.workspace, d.workspace_bytes = ws.data_ptr(), ws.numel()
+            out = torch.full((total_q, wl.Hq, wl.D), 7.0, dtype=torch.bfloat16, device=H.dev())
+            st = nb.dflash_block_attn(t["q"], t["k"], t["v"], t["pt"], t["ctx"], t["blk"], wl.Hq, wl.Hkv, wl.D,
+                                      t["causal"], wl.window, wl.scale, out, torch.cuda.current_stream().cuda_stream,
+                                      d)
+            assert st == nb.DFLASH_OK, nb.dflash_last_error_message()
+            torch.cuda.synchronize()
+            H.assert_parity(H.to_f64(out[:wl.total_q]), oracle.run_workload(wl), f"B=130 grid {nwg}")
+            assert torch.all(out[wl.total_q:] == 7.0), "rows of no request were written"
