@@ -115,6 +115,12 @@ constexpr int kMinTilesPerWg = 2;
 // slower).
 constexpr int kSegmentCharge = 3;
 constexpr int kSegmentChargeShort = 2;
+// Five row tiles at head_dim 512 (72-80 rows per unit): set-up plus epilogue take about
+// 3.6 tiles' time (4.2 + 4.5 us against 2.44 us per tile), so a charge of 4 balances the
+// runs that cross into a second unit.  The B = 4 x 9 global layer's call measured 1-2 us
+// faster with it in five A/B runs (0.8-2.0 us), 5 was level with 3, and the B = 8 x 9
+// global verify layer was level; at four row tiles (about 3.1 tiles of set-up) 3 stays.
+constexpr int kSegmentChargeWide = 4;
 constexpr int kChargeMinTiles = 16;
 constexpr size_t kAlign = 256;
 // Largest grid the automatic choice always merges split units in (besides the small steps
@@ -283,6 +289,8 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             groups = ((int64_t)desc->max_block_len * G + p->rmax - 1) / p->rmax;
         const int64_t tiles = (int64_t)Hkv * groups * (desc->total_kv_len / p->tk);
         p->ov = tiles >= (int64_t)kChargeMinTiles * P ? kSegmentCharge : kSegmentChargeShort;
+        if (p->ov == kSegmentCharge && p->row_tiles == 5 && p->Dp == 512)
+            p->ov = kSegmentChargeWide;
     }
     if (p->P > 1) {
         // [merge counters, a fixed layout for every grid (merge.h)]

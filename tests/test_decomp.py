@@ -32,7 +32,7 @@ def test_config_shapes(checker, name, P):
     k = ks[rng.integers(0, len(ks), size=cfg.B)] if len(ks) > 1 else np.full(cfg.B, ks[0])
     G = cfg.Hq // cfg.Hkv
     for rmax, tk in ((80, 32), (64, 32), (16, 16)):
-        for ov in (0, 2, 3):
+        for ov in (0, 2, 3, 4):
             run(checker, L, 1 + k, cfg.Hkv, G, cfg.window, rmax, tk, P, ov)
 
 
@@ -49,7 +49,7 @@ def test_random_edge_cases(checker):
         rmax = int(rng.choice([16, 32, 48, 64, 80]))
         tk = int(rng.choice([16, 32]))
         P = int(rng.integers(1, 60))
-        ov = int(rng.choice([0, 0, 1, 2, 3, 7]))
+        ov = int(rng.choice([0, 0, 1, 2, 3, 4, 7]))
         run(checker, L, n, Hkv, G, window, rmax, tk, P, ov)
 
 
