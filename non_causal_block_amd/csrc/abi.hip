@@ -329,13 +329,12 @@ int make_plan(const dflash_batch_desc* desc, int32_t Hq, int32_t Hkv, int32_t D,
             p->combine_rows = true;
             p->combine_wgs = (int)rows;
         }
-        // Up to head_dim 256 the rows-per-wave combine finds each row's pieces in the merge
-        // directory: one load instead of a pass over the request arrays, a reload of the
-        // row's lengths and the work-split arithmetic (calls: the causal window-1024 workload
-        // of 16 x 16 queries 43.8 -> 42.0 us, B = 8 x 9 at L ~ U[1024, 4096] 46.9 -> 46.3 us;
-        // A/B on one box).  At head_dim 512 (and in the workgroup-per-row combine,
-        // bound by its partial reads) it measured no faster, so those keep the request arrays.
-        p->use_dir = p->off_dir != 0 && !p->combine_rows && p->Dp <= 256;
+        // The combine finds each row's pieces in the merge directory: one load instead of a
+        // pass over the request arrays, a reload of the row's lengths and the work-split
+        // arithmetic (calls, A/B on one box: the causal window-1024 workload of 16 x 16
+        // queries 43.8 -> 42.0 us, B = 8 x 9 at L ~ U[1024, 4096] 46.9 -> 46.3 us, the
+        // head_dim-512 global layer at B = 4 x 9 128.1 -> 126.6 us).
+        p->use_dir = p->off_dir != 0;
     }
     return DFLASH_OK;
 }

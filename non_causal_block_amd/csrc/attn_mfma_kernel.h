@@ -205,10 +205,9 @@ __global__ __launch_bounds__(threads_for<DP>) void attn_mfma_kernel(AttnArgs a)
     // Otherwise V of the next tile is requested after this wave's S^T products, or, where a
     // wave owns two row tiles, after the first barrier.
     constexpr bool V_AFTER_BARRIER = !LATE_V && RT > WAVES;
-    // Instances that write the merge directory (AttnArgs::dir; the planner passes one only
-    // up to head_dim 256): at head_dim 512 the directory measured no faster in the combine,
-    // and its epilogue checks alone cost the attention kernel about 1% on C3.
-    constexpr bool DIR = DP <= 256;
+    // The merge directory (AttnArgs::dir) is written by every instance when the planner
+    // passes one (every launch whose partials the combine kernel merges).
+    constexpr bool DIR = true;
 
     if (a.dbg && *a.dbg != 0u)
         return;  // debug checks found a bad device-side value: touch nothing

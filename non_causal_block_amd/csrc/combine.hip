@@ -106,8 +106,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a)
 // many ways (16 to 30 pieces at the long-context head_dim-512 shapes) then needs one
 // load round per wave instead of two for a single wave; the four partial sums, each
 // with its own running max, meet in LDS and wave 0 writes the row.
-template <int PPS>
-__global__ __launch_bounds__(256) void combine_row_kernel(CombineArgs a)
+// DIRK: the row's pieces come from the attention kernel's merge directory (a.dir), else
+// from the request arrays.  Both instances are held to at most 96 registers (5 waves per
+// SIMD; the directory instance needs 70), so that at least 1280 workgroups fit on the
+// chip at once (C3's 1152 rows): at 4 waves per SIMD the last rows wait for a second
+// round (C3's call 1.7 us slower, A/B on one box).
+template <int PPS, bool DIRK>
+__global__ __launch_bounds__(256, 5) void combine_row_kernel(CombineArgs a)
 {
     constexpr int NW = kCombineWavesPerWg;
     __shared__ float s_m[NW], s_w[NW];
@@ -121,24 +126,39 @@ __global__ __launch_bounds__(256) void combine_row_kernel(CombineArgs a)
     const int64_t t = row / a.Hq;
     const int32_t h = (int32_t)(row % a.Hq);
 
-    int32_t r;
-    int64_t qstart, rbase, total;
-    wave_locate_token(a.ctx_lens, a.block_lens, d, t, r, qstart, rbase, total);
-    if (r >= d.B)
-        return;  // token past the real total (the same for every wave of the workgroup)
-    const int32_t L = a.ctx_lens[r];
-    const int32_t n = a.block_lens[r];
-    const ReqGeom g = req_geom(L, n, d);
-    const int64_t tpw = tiles_per_wg(total, d.P);
-    const int32_t rowreq = (int32_t)(t - qstart) * d.G + h % d.G;
-    const int32_t rin = rowreq % d.rmax;
-    const int32_t unit = (h / d.G) * g.ngroups + rowreq / d.rmax;
-    const int64_t us = rbase + (int64_t)unit * g.uwork;
-    int64_t kf, kl;
-    unit_pieces(g, us, d.ov, tpw, kf, kl);
-    if (kf == kl)
-        return;  // finished inside one attention workgroup: already written
-    const int64_t np = kl - kf + 1;
+    int64_t kf, np, us, tpw;
+    int32_t rin;
+    if constexpr (DIRK) {
+        // pieces kf .. kf+np-1; piece_slot(k, kf + slot0, 1) then gives the first piece's
+        // slot and slot 0 for the later ones
+        const DirEntry e = dir_unpack(a.dir[row]);
+        if (e.np <= 1 || e.kf + e.np > d.P)
+            return;  // no request's row, or finished whole (always within the grid)
+        kf = e.kf;
+        np = e.np;
+        us = kf + e.slot0;
+        tpw = 1;
+        rin = e.rin;
+    } else {
+        int32_t r;
+        int64_t qstart, rbase, total;
+        wave_locate_token(a.ctx_lens, a.block_lens, d, t, r, qstart, rbase, total);
+        if (r >= d.B)
+            return;  // token past the real total (the same for every wave of the workgroup)
+        const int32_t L = a.ctx_lens[r];
+        const int32_t n = a.block_lens[r];
+        const ReqGeom g = req_geom(L, n, d);
+        tpw = tiles_per_wg(total, d.P);
+        const int32_t rowreq = (int32_t)(t - qstart) * d.G + h % d.G;
+        rin = rowreq % d.rmax;
+        const int32_t unit = (h / d.G) * g.ngroups + rowreq / d.rmax;
+        us = rbase + (int64_t)unit * g.uwork;
+        int64_t kl;
+        unit_pieces(g, us, d.ov, tpw, kf, kl);
+        if (kf == kl)
+            return;  // finished inside one attention workgroup: already written
+        np = kl - kf + 1;
+    }
     const int64_t cnt = np > wave ? (np - wave + NW - 1) / NW : 0;  // this wave's pieces
     const int32_t d0 = lane * 8;
     const bool dlive = d0 < a.D;
@@ -246,7 +266,10 @@ hipError_t launch_combine_rows(const CombineArgs& a, hipStream_t stream)
 {
     if (a.total_rows <= 0 || a.total_rows > 0x7fffffff || a.Dp > 512)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((combine_row_kernel<8>), dim3((unsigned)a.total_rows), dim3(256), 0, stream, a);
+    if (a.dir)
+        hipLaunchKernelGGL((combine_row_kernel<8, true>), dim3((unsigned)a.total_rows), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((combine_row_kernel<8, false>), dim3((unsigned)a.total_rows), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

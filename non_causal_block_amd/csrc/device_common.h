@@ -293,9 +293,9 @@ struct AttnArgs {
     int32_t max_pages_per_req;
     float scale_log2;  // scale * log2(e)
     const uint32_t* dbg;  // debug-check state or nullptr: when it is non-zero the kernel does nothing
-    // Merge directory for the rows-per-wave combine kernel, one entry per output row
-    // (token * Hq + q-head) of [0, total_rows): written in full by every launch whose
-    // partials that kernel merges, nullptr otherwise.  Entry (x, y): x = first piece's workgroup kf | that
+    // Merge directory for the combine kernel, one entry per output row (token * Hq +
+    // q-head) of [0, total_rows): written in full by every launch whose partials that
+    // kernel merges, nullptr otherwise.  Entry (x, y): x = first piece's workgroup kf | that
     // piece's slot << 31; y = pieces np (bits 0-23) | the row's index inside its unit << 24.
     // np = 1: the unit was finished whole (nothing to merge); np = 0: a row of no request.
     uint2* dir;
@@ -343,7 +343,7 @@ struct CombineArgs {
     int64_t total_rows;  // total_q hint * Hq
     const uint32_t* dbg;  // as in AttnArgs
     // the attention kernel's merge directory (AttnArgs::dir), or nullptr: then each row's
-    // pieces are derived from the request arrays (combine_row_kernel always does that)
+    // pieces are derived from the request arrays
     const uint2* dir;
 };
 

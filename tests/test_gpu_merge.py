@@ -156,17 +156,18 @@ def test_grid_larger_than_the_chip(D):
     assert not _counters(ws).any()
 
 
+@pytest.mark.parametrize("D", [256, 512])
 @pytest.mark.parametrize("nwg", [24, 200])
-def test_combine_directory_rows_of_no_request(nwg):
+def test_combine_directory_rows_of_no_request(nwg, D):
     """The combine kernel finds each output row's pieces in a directory that the attention
     kernel writes on every call (one entry per row of the total_q hint).  Rows past the
     blocks' sum belong to no request: a call must leave them alone even when an earlier
     call on the same workspace had real rows there, and a call whose blocks are all empty
-    must leave every row alone.  Head_dim 256 (the directory's instances); 24 workgroups
-    split each unit a few ways, 200 many."""
-    big = workloads.build(3, 8, 2, 256, [3000, 900, 2000], [9, 9, 9], [0, 1, 0], seed=51)
-    small = workloads.build(2, 8, 2, 256, [2500, 1200], [9, 4], [1, 0], seed=52)
-    empty = workloads.build(2, 8, 2, 256, [300, 100], [0, 0], [0, 0], seed=53)
+    must leave every row alone.  24 workgroups split each unit a few ways (rows per wave
+    in the combine), 200 many (at head_dim 512, a workgroup per row)."""
+    big = workloads.build(3, 8, 2, D, [3000, 900, 2000], [9, 9, 9], [0, 1, 0], seed=51)
+    small = workloads.build(2, 8, 2, D, [2500, 1200], [9, 4], [1, 0], seed=52)
+    empty = workloads.build(2, 8, 2, D, [300, 100], [0, 0], [0, 0], seed=53)
     extra = 5
 
     def call(wl, t, ws, total_q, out):
